@@ -1,0 +1,339 @@
+/*
+ * kvrec_oracle.c - plain CPU reference of the paged KV-record codec.
+ *
+ * TEST INFRASTRUCTURE: see kvrec_oracle.h. Built with
+ *   gcc -O2 -ffp-contract=off -fno-fast-math
+ * so every float operation written here is one IEEE-754 binary32 (or
+ * binary64) operation rounded to nearest-even, with no fused multiply-add.
+ *
+ * Structure: each token is processed on its own, in the order the pages
+ * state the steps (skip, widen, rotate, per-group amax, scale, encode,
+ * store). There is no blocking, vectorisation or reordering.
+ *
+ * Citation keys are defined in kvrec_oracle.h.
+ */
+#include "kvrec_oracle.h"
+
+#include <math.h>
+#include <string.h>
+
+enum {
+  HEAD_DIM = 512,  /* latent width of one token  [MXFP8 record, 功能与动机] */
+  ROPE_DIM = 64,   /* rotated tail dims          [KV-only op, 实现拆解 1]  */
+  NOPE_DIM = 448,  /* HEAD_DIM - ROPE_DIM                                  */
+  HALF_ROPE = 32,
+  V41_RECORD = 528,
+  V4_RECORD = 584,
+};
+
+/* ------------------------------------------------------------------------ */
+/* e4m3fn ("float8e4nv" in the excerpt of [MXFP8 record, 关键源码片段]).     */
+/* OCP FP8 E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; no  */
+/* infinities; exponent 1111 with mantissa 111 is NaN, so the largest       */
+/* finite magnitude is 1.75 * 2^8 = 448.                                    */
+/* ------------------------------------------------------------------------ */
+double orc_e4m3_value(uint8_t code) {
+  int sign = code >> 7;
+  int expo = (code >> 3) & 15;
+  int mant = code & 7;
+  double mag;
+  if (expo == 15 && mant == 7) return NAN;
+  if (expo == 0)
+    mag = ldexp((double)mant, -9);            /* (mant/8) * 2^(1-7)        */
+  else
+    mag = ldexp((double)(8 + mant), expo - 10); /* (1+mant/8) * 2^(expo-7) */
+  return sign ? -mag : mag;
+}
+
+/* Round to nearest representable e4m3fn value; on a tie take the value whose
+ * code is even (even mantissa); saturate magnitudes >= 448 to 448 (the
+ * excerpt clamps to +-448 before the cast [MXFP8 record, 关键源码片段]).
+ * The sign bit is copied, so -0 encodes as 0x80. */
+uint8_t orc_e4m3_encode(double y) {
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  double a = fabs(y);
+  int lo, hi;
+  if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+  /* Non-negative codes 0x00..0x7E are ordered by value. Find the bracket
+   * value(lo) <= a < value(hi) by bisection. */
+  lo = 0x00;
+  hi = 0x7E;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (orc_e4m3_value((uint8_t)mid) <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  {
+    double below = a - orc_e4m3_value((uint8_t)lo); /* exact in binary64 */
+    double above = orc_e4m3_value((uint8_t)hi) - a;
+    int code;
+    if (below < above)
+      code = lo;
+    else if (above < below)
+      code = hi;
+    else
+      code = (lo % 2 == 0) ? lo : hi;
+    return (uint8_t)(sign | code);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* bfloat16: binary32 with the low 16 fraction bits dropped (8 significant  */
+/* bits, same exponent range).                                              */
+/* ------------------------------------------------------------------------ */
+uint16_t orc_bf16_round(double x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+  double a = fabs(x);
+  int e2;
+  int unit;    /* a lies in [2^unit, 2^(unit+1)) */
+  int quantum; /* spacing of bf16 values there: 2^quantum */
+  double steps, whole, frac, rounded, value;
+  float f;
+  uint32_t bits;
+
+  if (a == 0.0) return sign;
+  (void)frexp(a, &e2); /* a = m * 2^e2, m in [0.5, 1) */
+  unit = e2 - 1;
+  quantum = (unit < -126 ? -126 : unit) - 7; /* subnormals share 2^-133   */
+  steps = ldexp(a, -quantum);                /* exact: power-of-two scale */
+  whole = floor(steps);
+  frac = steps - whole;
+  if (frac > 0.5)
+    rounded = whole + 1.0;
+  else if (frac < 0.5)
+    rounded = whole;
+  else
+    rounded = (fmod(whole, 2.0) == 0.0) ? whole : whole + 1.0;
+  value = ldexp(rounded, quantum);
+  if (value >= 0x1p128) return (uint16_t)(sign | 0x7F80); /* +-inf */
+  f = (float)value; /* exact: value has <= 8 significant bits */
+  memcpy(&bits, &f, sizeof bits);
+  return (uint16_t)(sign | (bits >> 16));
+}
+
+/* ------------------------------------------------------------------------ */
+/* UE8M0 group scale. The excerpt computes ceil(log2(amax / 448)) and stores */
+/* it biased by 127 [MXFP8 record, 关键源码片段]. Read as exact real          */
+/* arithmetic: the smallest integer e with amax <= 448 * 2^e, so that every  */
+/* |x| * 2^-e in the group is <= 448. Clamped to [-127, 127] (byte 0..254).  */
+/* amax == 0 (an all-zero group) takes e = 0, byte 127 (no 1e-4 floor).      */
+/* ------------------------------------------------------------------------ */
+int orc_scale_exponent(float amax) {
+  int e;
+  if (amax == 0.0f) return 0;
+  for (e = -127; e < 127; ++e)
+    if ((double)amax <= ldexp(448.0, e)) return e;
+  return 127;
+}
+
+/* bf16 bits -> binary32 value (exact widening). */
+static float widen_bf16(uint16_t h) {
+  uint32_t bits = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return f;
+}
+
+/* fp32 RoPE of one latent row: dims 0..447 pass through untouched; the tail
+ * dims 448..511 are rotated with the NeoX half-split pairing (448+i, 480+i),
+ * cos = row[i], sin = row[32+i], products first and then one add/subtract,
+ * each a separate binary32 operation:
+ *   r[448+i] = (x1*c) - (x2*s),   r[480+i] = (x2*c) + (x1*s).
+ * The table layout (32 cos then 32 sin, fp32 [max_pos, 64]) is from
+ * [KV-only op, 实现拆解 1]; the product-then-add order is the one in the
+ * excerpt of [MXFP8 record, 关键源码片段]. */
+static void rope_row(const uint16_t *kv_row, const float *cs_row, float *r) {
+  int d, i;
+  for (d = 0; d < NOPE_DIM; ++d) r[d] = widen_bf16(kv_row[d]);
+  for (i = 0; i < HALF_ROPE; ++i) {
+    float x1 = widen_bf16(kv_row[NOPE_DIM + i]);
+    float x2 = widen_bf16(kv_row[NOPE_DIM + HALF_ROPE + i]);
+    float c = cs_row[i];
+    float s = cs_row[HALF_ROPE + i];
+    float x1c = x1 * c;
+    float x2s = x2 * s;
+    float x2c = x2 * c;
+    float x1s = x1 * s;
+    r[NOPE_DIM + i] = x1c - x2s;
+    r[NOPE_DIM + HALF_ROPE + i] = x2c + x1s;
+  }
+}
+
+/* Quantise dims [first, first+width) of r as one group: returns the scale
+ * byte and writes width e4m3 codes. The element code is the e4m3fn value
+ * nearest to the exact product r * 2^-e. */
+static uint8_t quantise_group(const float *r, int first, int width,
+                              uint8_t *codes) {
+  float amax = 0.0f;
+  int d, e;
+  for (d = first; d < first + width; ++d)
+    if (fabsf(r[d]) > amax) amax = fabsf(r[d]);
+  e = orc_scale_exponent(amax);
+  for (d = first; d < first + width; ++d)
+    codes[d - first] = orc_e4m3_encode(ldexp((double)r[d], -e));
+  return (uint8_t)(e + 127);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Insert.                                                                  */
+/*                                                                          */
+/* Token count and slot skip: [KV-only op, 实现拆解 1 and 风险与影响];        */
+/* negative slot -> nothing written [MXFP8 record, 关键源码片段].             */
+/* Guard (a reading): a slot >= num_blocks*block_size or a position outside  */
+/* [0, max_pos) also skips the token.                                       */
+/*                                                                          */
+/* MXFP8 record (528 B/token) [MXFP8 record, 功能与动机 and 关键源码片段]:    */
+/*   page = slot / block_size, off = slot % block_size;                     */
+/*   512 codes at page + off*512 (all dims, RoPE dims after rotation);       */
+/*   16 UE8M0 bytes (one per 32 dims) at page + block_size*512 + off*16.     */
+/*                                                                          */
+/* Legacy record (584 B/token) [MXFP8 record, 功能与动机]: 448 NoPE dims as  */
+/* e4m3 with 7 UE8M0 scales over 64-dim groups, the 64 rotated RoPE dims as */
+/* bf16, 576 B data row then an 8 B scale row (7 scales + 1 pad). Reading:  */
+/* data region first (rows of 576 B: codes then little-endian bf16), then   */
+/* the scale region (rows of 8 B, pad byte written as 0), as for the MXFP8  */
+/* record's data-then-scale page.                                           */
+/* ------------------------------------------------------------------------ */
+int orc_insert(const uint16_t *kv, int64_t n, uint8_t *cache,
+               int64_t num_blocks, int64_t page_stride, int32_t block_size,
+               int32_t record, const int64_t *slot_mapping,
+               const int64_t *positions, const float *cos_sin_cache,
+               int64_t max_pos) {
+  int64_t t;
+  int64_t total_slots = num_blocks * (int64_t)block_size;
+  if (record != V41_RECORD && record != V4_RECORD) return -1;
+
+  for (t = 0; t < n; ++t) {
+    float r[HEAD_DIM];
+    int64_t slot = slot_mapping[t];
+    int64_t pos = positions[t];
+    int64_t page, off;
+    uint8_t *pg;
+    int g, i;
+
+    if (slot < 0 || slot >= total_slots) continue;
+    if (pos < 0 || pos >= max_pos) continue;
+
+    rope_row(kv + t * HEAD_DIM, cos_sin_cache + pos * ROPE_DIM, r);
+
+    page = slot / block_size;
+    off = slot % block_size;
+    pg = cache + page * page_stride;
+
+    if (record == V41_RECORD) {
+      uint8_t *data = pg + off * 512;
+      uint8_t *scales = pg + (int64_t)block_size * 512 + off * 16;
+      for (g = 0; g < 16; ++g)
+        scales[g] = quantise_group(r, g * 32, 32, data + g * 32);
+    } else {
+      uint8_t *data = pg + off * 576;
+      uint8_t *scales = pg + (int64_t)block_size * 576 + off * 8;
+      for (g = 0; g < 7; ++g)
+        scales[g] = quantise_group(r, g * 64, 64, data + g * 64);
+      scales[7] = 0;
+      for (i = 0; i < ROPE_DIM; ++i) {
+        uint16_t h = orc_bf16_round((double)r[NOPE_DIM + i]);
+        data[NOPE_DIM + 2 * i] = (uint8_t)(h & 0xFF);
+        data[NOPE_DIM + 2 * i + 1] = (uint8_t)(h >> 8);
+      }
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gather (dequantise to bf16). Index = page * block_size + offset; a       */
+/* negative index marks an invalid entry [FlashMLA, sparse decode           */
+/* integration notes] and yields a row of +0. Reading: an index >=          */
+/* num_blocks*block_size is treated the same way.                           */
+/* Element: bf16 nearest to e4m3(code) * 2^(scale - 127). The RoPE dims are */
+/* returned rotated. Legacy record: dims 448..511 are the stored bf16.      */
+/* [MXFP8 record, 实现拆解 4]: one gather parameterised by the fp8 width    */
+/* (448 or 512), the group size (64 or 32) and a bf16 tail.                 */
+/* ------------------------------------------------------------------------ */
+int orc_gather(const uint8_t *cache, int64_t num_blocks, int64_t page_stride,
+               int32_t block_size, int32_t record,
+               const int32_t *token_indices, int64_t n, uint16_t *out) {
+  int64_t j;
+  int64_t total_slots = num_blocks * (int64_t)block_size;
+  if (record != V41_RECORD && record != V4_RECORD) return -1;
+
+  for (j = 0; j < n; ++j) {
+    int64_t idx = token_indices[j];
+    uint16_t *row = out + j * HEAD_DIM;
+    int64_t page, off;
+    const uint8_t *pg;
+    int d;
+
+    if (idx < 0 || idx >= total_slots) {
+      for (d = 0; d < HEAD_DIM; ++d) row[d] = 0;
+      continue;
+    }
+    page = idx / block_size;
+    off = idx % block_size;
+    pg = cache + page * page_stride;
+
+    if (record == V41_RECORD) {
+      const uint8_t *data = pg + off * 512;
+      const uint8_t *scales = pg + (int64_t)block_size * 512 + off * 16;
+      for (d = 0; d < HEAD_DIM; ++d) {
+        double v = orc_e4m3_value(data[d]) * ldexp(1.0, (int)scales[d / 32] - 127);
+        row[d] = orc_bf16_round(v);
+      }
+    } else {
+      const uint8_t *data = pg + off * 576;
+      const uint8_t *scales = pg + (int64_t)block_size * 576 + off * 8;
+      for (d = 0; d < NOPE_DIM; ++d) {
+        double v = orc_e4m3_value(data[d]) * ldexp(1.0, (int)scales[d / 64] - 127);
+        row[d] = orc_bf16_round(v);
+      }
+      for (d = 0; d < ROPE_DIM; ++d)
+        row[NOPE_DIM + d] = (uint16_t)(data[NOPE_DIM + 2 * d] |
+                                       (data[NOPE_DIM + 2 * d + 1] << 8));
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Batch forms used by the pin tests.                                       */
+/* ------------------------------------------------------------------------ */
+void orc_e4m3_encode_f32(const float *y, int64_t n, uint8_t *out) {
+  int64_t i;
+  for (i = 0; i < n; ++i) out[i] = orc_e4m3_encode((double)y[i]);
+}
+
+void orc_e4m3_encode_bits(uint32_t first_bits, int64_t n, uint8_t *out) {
+  int64_t i;
+  for (i = 0; i < n; ++i) {
+    uint32_t bits = first_bits + (uint32_t)i;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    out[i] = orc_e4m3_encode((double)f);
+  }
+}
+
+void orc_e4m3_value_all(double *out256) {
+  int c;
+  for (c = 0; c < 256; ++c) out256[c] = orc_e4m3_value((uint8_t)c);
+}
+
+void orc_bf16_round_f32(const float *x, int64_t n, uint16_t *out) {
+  int64_t i;
+  for (i = 0; i < n; ++i) out[i] = orc_bf16_round((double)x[i]);
+}
+
+void orc_scale_exponent_f32(const float *amax, int64_t n, int32_t *out) {
+  int64_t i;
+  for (i = 0; i < n; ++i) out[i] = orc_scale_exponent(amax[i]);
+}
+
+void orc_rope_rows(const uint16_t *kv, int64_t n, const int64_t *positions,
+                   const float *cos_sin_cache, float *out) {
+  int64_t t;
+  for (t = 0; t < n; ++t)
+    rope_row(kv + t * HEAD_DIM, cos_sin_cache + positions[t] * ROPE_DIM,
+             out + t * HEAD_DIM);
+}

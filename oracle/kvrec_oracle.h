@@ -1,0 +1,82 @@
+/*
+ * kvrec_oracle.h - plain CPU reference of the paged KV-record codec.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library. The product path (libkvrec.so)
+ * never links, loads or calls it, and shares no code, header, table or
+ * helper with it.
+ *
+ * Every function is a direct, slow statement of what the pages define:
+ *   [MXFP8 record]  vLLM PR #56893 report, "[Model][DSv4.1] Store the whole KV
+ *                   in MXFP8 (FlashMLA V4.1 record)"
+ *   [KV-only op]    vLLM PR #56441 report, "[Perf][DSpark] Add KV-only context
+ *                   insertion across V4.1 cache formats"
+ *   [FlashMLA]      article page "deepseek-ai/FlashMLA" (ssnai.com)
+ * Where the pages leave a step open, the reading taken is stated at the
+ * function. All integers are host-endian (little-endian x86-64).
+ */
+#ifndef KVREC_ORACLE_H
+#define KVREC_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- element codecs ---------------------------------------------------- */
+
+/* Exact real value of an OCP e4m3fn code (NaN for 0x7F / 0xFF). */
+double orc_e4m3_value(uint8_t code);
+
+/* e4m3fn code nearest to y, ties to the even code, |y| >= 448 -> +-448. */
+uint8_t orc_e4m3_encode(double y);
+
+/* bfloat16 bits nearest to x, ties to even, beyond the largest finite
+ * rounding threshold -> +-inf. */
+uint16_t orc_bf16_round(double x);
+
+/* Smallest integer e with amax <= 448 * 2^e, clamped to [-127, 127];
+ * amax == 0 gives 0. */
+int orc_scale_exponent(float amax);
+
+/* ---- the two operations ------------------------------------------------ */
+
+/* Insert n tokens into a host copy of the paged cache.
+ *   kv            bf16 bits [n, 512], row-major
+ *   cache         byte 0 of page 0; num_blocks pages page_stride bytes apart
+ *   block_size    tokens per page
+ *   record        528 (MXFP8 record) or 584 (legacy record)
+ *   slot_mapping  [n] int64; negative -> token skipped
+ *   positions     [n] int64; row of cos_sin_cache to use
+ *   cos_sin_cache fp32 [max_pos, 64]: 32 cos values then 32 sin values
+ * Returns 0, or -1 if record is not 528/584. */
+int orc_insert(const uint16_t *kv, int64_t n, uint8_t *cache,
+               int64_t num_blocks, int64_t page_stride, int32_t block_size,
+               int32_t record, const int64_t *slot_mapping,
+               const int64_t *positions, const float *cos_sin_cache,
+               int64_t max_pos);
+
+/* Gather n records back to bf16 rows.
+ *   token_indices [n] int32, page * block_size + offset; negative -> zeros
+ *   out           bf16 bits [n, 512]
+ * Returns 0, or -1 if record is not 528/584. */
+int orc_gather(const uint8_t *cache, int64_t num_blocks, int64_t page_stride,
+               int32_t block_size, int32_t record,
+               const int32_t *token_indices, int64_t n, uint16_t *out);
+
+/* ---- batch forms of the element codecs, for the pin tests -------------- */
+
+void orc_e4m3_encode_f32(const float *y, int64_t n, uint8_t *out);
+void orc_e4m3_encode_bits(uint32_t first_bits, int64_t n, uint8_t *out);
+void orc_e4m3_value_all(double *out256);
+void orc_bf16_round_f32(const float *x, int64_t n, uint16_t *out);
+void orc_scale_exponent_f32(const float *amax, int64_t n, int32_t *out);
+void orc_rope_rows(const uint16_t *kv, int64_t n, const int64_t *positions,
+                   const float *cos_sin_cache, float *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVREC_ORACLE_H */
