@@ -1,0 +1,155 @@
+/*
+ * kvrec.h - C ABI of the MI355X (gfx950) paged KV-record codec.
+ *
+ * Two operations on a paged uint8 KV cache holding one 512-dim MLA latent
+ * per token:
+ *
+ *   kvrec_insert  fused fp32 RoPE on the 64 tail dims + MXFP8 (or legacy)
+ *                 quantisation + paged store of the token's record;
+ *   kvrec_gather  the inverse: paged read + dequantisation to bf16 rows.
+ *
+ * Sources (page titles; sections named as on the pages):
+ *   [MXFP8 record] vLLM PR #56893 report, "[Model][DSv4.1] Store the whole KV
+ *                  in MXFP8 (FlashMLA V4.1 record)"
+ *   [KV-only op]   vLLM PR #56441 report, "[Perf][DSpark] Add KV-only context
+ *                  insertion across V4.1 cache formats"
+ *   [FlashMLA]     article page "deepseek-ai/FlashMLA" (ssnai.com)
+ *
+ * Conventions for every call:
+ *   - Pointers marked (device) are HIP device memory of the current device;
+ *     kvrec_cache is a host struct describing device memory.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the legacy
+ *     default stream). The library allocates nothing, keeps no state and
+ *     never synchronises. The caller owns every buffer.
+ *   - Every argument check runs on the host before any launch; on error the
+ *     call returns a negative kvrec_status and nothing is launched or
+ *     written. The library never throws or aborts across this ABI.
+ *   - Device-resident values are not inspected on the host. Preconditions
+ *     the caller keeps: non-negative slots distinct within one insert; kv
+ *     finite with |x| < 2^127 (so the rotation cannot overflow); kv, out and
+ *     token_indices do not overlap the cache. As a memory-safety guard the
+ *     kernels skip a token whose slot is >= num_blocks * block_size or whose
+ *     position is outside [0, max_pos), and gather a zero row for an index
+ *     >= num_blocks * block_size.
+ */
+#ifndef KVREC_H
+#define KVREC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Latent width and rotated tail ([MXFP8 record] 功能与动机; [KV-only op]
+ * 实现拆解 1: kv is bf16 [tokens, 512], cos_sin_cache fp32 [max_pos, 64]). */
+#define KVREC_HEAD_DIM 512
+#define KVREC_ROPE_DIM 64
+
+/* Record widths in bytes per token, which also select the format
+ * ([MXFP8 record] 功能与动机 and 实现拆解 4; [KV-only op] 实现拆解 1: the
+ * packed cache's last dimension must be 528 or 584):
+ *   528  MXFP8 record: 512 e4m3fn codes (RoPE dims rotated, then quantised)
+ *        + 16 UE8M0 scales, one per 32 dims; page alignment 512 B.
+ *   584  legacy record: 448 e4m3fn codes of the NoPE dims + 64 rotated RoPE
+ *        dims as bf16 (576 B data row) + 7 UE8M0 scales over 64-dim groups
+ *        + 1 pad byte (8 B scale row); page alignment 576 B. */
+#define KVREC_RECORD_MXFP8 528
+#define KVREC_RECORD_LEGACY 584
+
+typedef enum kvrec_status {
+  KVREC_OK = 0,
+  KVREC_ERR_NULL = -1,        /* a required pointer is NULL               */
+  KVREC_ERR_RECORD = -2,      /* record not 528/584, or != cache's record */
+  KVREC_ERR_BLOCK_SIZE = -3,  /* block_size < 1, or != cache's block_size */
+  KVREC_ERR_PAGE_STRIDE = -4, /* page stride not a multiple of the record's
+                                 alignment, or < block_size * record      */
+  KVREC_ERR_ALIGNMENT = -5,   /* a pointer is not aligned as stated below */
+  KVREC_ERR_SIZE = -6,        /* negative count, max_pos < 1, or a size
+                                 beyond what the kernels index            */
+  KVREC_ERR_HIP = -7          /* the HIP launch reported an error         */
+} kvrec_status;
+
+/* A paged cache: num_blocks pages, page_stride bytes apart, each holding
+ * block_size records laid out as a data region (block_size rows of 512 B, or
+ * 576 B for the legacy record) followed by a scale region (block_size rows of
+ * 16 B, or 8 B) and then padding up to page_stride ([MXFP8 record] 实现拆解 4
+ * and 关键源码片段: data at page + off*512, scales at page + block*512 +
+ * off*16). A token in slot s lives in page s / block_size at offset
+ * s % block_size. */
+typedef struct kvrec_cache {
+  void *base;          /* (device) byte 0 of page 0; 16-B aligned          */
+  int64_t num_blocks;  /* pages, >= 0                                      */
+  int64_t page_stride; /* bytes between pages; a multiple of 512 (528) or
+                          576 (584) and >= block_size * record             */
+  int32_t block_size;  /* tokens per page, >= 1                            */
+  int32_t record;      /* 528 or 584                                       */
+} kvrec_cache;
+
+/* hipStream_t, passed opaquely so this header needs no HIP headers. */
+typedef void *kvrec_stream;
+
+/* Page stride for a record and block size: block_size * record rounded up
+ * to the record's alignment (512 or 576). Host-only, pure.
+ * Returns KVREC_OK and writes *page_stride_out, or KVREC_ERR_NULL,
+ * KVREC_ERR_RECORD, KVREC_ERR_BLOCK_SIZE. */
+int kvrec_page_stride(int32_t record, int32_t block_size, int64_t *page_stride_out);
+
+/* Insert num_tokens tokens ([KV-only op] 实现拆解 1 and 2: kv, k_cache,
+ * slot_mapping, positions, cos_sin_cache, cache block size; the record is
+ * read from the cache's last dimension).
+ *
+ *   kv            (device) bf16 [num_tokens, 512], rows contiguous; 16-B
+ *                 aligned; read only.
+ *   num_tokens    >= 0, < 2^31; 0 returns KVREC_OK without a launch.
+ *   k_cache       host descriptor of the cache written in place.
+ *   slot_mapping  (device) int64 [num_tokens]; 8-B aligned. A negative slot
+ *                 skips its token: nothing is written for it.
+ *   positions     (device) int64 [num_tokens]; 8-B aligned; the row of
+ *                 cos_sin_cache for each token.
+ *   cos_sin_cache (device) fp32 [max_pos, 64]: 32 cos values then 32 sin
+ *                 values per row; 16-B aligned.
+ *   max_pos       rows of cos_sin_cache, >= 1.
+ *   block_size    must equal k_cache->block_size (cross-check, as the page's
+ *                 op keeps k_cache.size(1) == cache_block_size).
+ *   record        must equal k_cache->record.
+ *
+ * Per token, in order: RoPE on dims 448..511 in fp32 with pairs
+ * (448+i, 480+i), r1 = x1*c - x2*s and r2 = x2*c + x1*s, each product and
+ * the add rounded separately (no fused multiply-add); dims 0..447 unchanged.
+ * MXFP8: for each 32-dim group, amax = max |r|, e = the smallest integer with
+ * amax <= 448 * 2^e clamped to [-127, 127] (e = 0 when amax == 0), scale
+ * byte e + 127, codes = e4m3fn(r * 2^-e) rounded to nearest even. Legacy: the
+ * same over seven 64-dim NoPE groups, and the rotated tail as bf16 (nearest
+ * even). Only the token's record bytes are written: page padding, other
+ * slots and skipped tokens keep their bytes.
+ * ([MXFP8 record] 功能与动机, 实现拆解 3 and 关键源码片段.) */
+int kvrec_insert(const void *kv, int64_t num_tokens, const kvrec_cache *k_cache,
+                 const int64_t *slot_mapping, const int64_t *positions,
+                 const float *cos_sin_cache, int64_t max_pos, int32_t block_size,
+                 int32_t record, kvrec_stream stream);
+
+/* Gather num_indices records back to bf16 rows ([MXFP8 record] 实现拆解 4:
+ * one gather parameterised by the record; [FlashMLA]: index =
+ * page * block_size + offset, -1 marks an invalid entry).
+ *
+ *   k_cache        host descriptor of the cache; read only.
+ *   token_indices  (device) int32 [num_indices]; 4-B aligned. A negative
+ *                  index gives a row of +0.
+ *   num_indices    >= 0, < 2^31; 0 returns KVREC_OK without a launch.
+ *   out            (device) bf16 [num_indices, 512]; 16-B aligned; written.
+ *
+ * Element d of a valid row is the bf16 nearest to e4m3fn(code_d) *
+ * 2^(scale - 127) (exact whenever the scale byte is >= 3); the RoPE dims
+ * come back rotated. Legacy record: dims 448..511 are the stored bf16. */
+int kvrec_gather(const kvrec_cache *k_cache, const int32_t *token_indices,
+                 int64_t num_indices, void *out, kvrec_stream stream);
+
+/* Static string naming a kvrec_status (never NULL). */
+const char *kvrec_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVREC_H */

@@ -1,0 +1,23 @@
+"""MI355X (gfx950) paged KV-record codec: fused RoPE + MXFP8 quantise +
+paged insert, and the paged dequantise-and-gather, for 512-dim MLA latent KV.
+
+The compute lives in ``libkvrec.so`` (HIP kernels behind the C ABI of
+``include/kvrec.h``); :mod:`.binding` marshals torch tensors into it. The
+library is loaded on first use, so importing this package (for instance for
+:mod:`.workloads`) needs neither a GPU nor a built library, while every
+compute call fails loudly without them.
+"""
+from .binding import (  # noqa: F401
+    HEAD_DIM,
+    RECORD_LEGACY,
+    RECORD_MXFP8,
+    ROPE_DIM,
+    KvrecError,
+    alloc_cache,
+    cache_descriptor,
+    kvrec_gather,
+    kvrec_insert,
+    kvrec_page_stride,
+    kvrec_status_str,
+    load_library,
+)

@@ -1,0 +1,204 @@
+"""Thin Python binding over ``libkvrec.so`` (the C ABI in include/kvrec.h).
+
+Argument marshalling only: every step of insert and gather runs in the HIP
+kernels behind the C ABI. PyTorch supplies device memory and the current
+stream. There is no CPU or PyTorch fallback: if the library is not built, or
+no GPU is present, every compute call raises.
+
+Shapes follow the page's KV-only op ([KV-only op] 实现拆解 1; page title
+"[Perf][DSpark] Add KV-only context insertion across V4.1 cache formats"):
+
+* ``kv``             bf16 ``[tokens, 512]`` contiguous (not modified)
+* ``k_cache``        uint8 ``[num_blocks, block_size, record]`` with
+                     ``stride(2) == 1`` and ``stride(1) == record``; the
+                     record (528 or 584) is read from the last dimension and
+                     the page stride from ``stride(0)`` (a padded stride is
+                     expressed with ``as_strided``; see :func:`alloc_cache`)
+* ``slot_mapping``   int64 ``[tokens]`` (token count = its length)
+* ``positions``      int64 covering every token
+* ``cos_sin_cache``  fp32 ``[max_pos, 64]`` (32 cos then 32 sin)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvrec.so")
+
+HEAD_DIM = 512
+ROPE_DIM = 64
+RECORD_MXFP8 = 528
+RECORD_LEGACY = 584
+
+KVREC_OK = 0
+STATUS_NAMES = {
+    0: "KVREC_OK", -1: "KVREC_ERR_NULL", -2: "KVREC_ERR_RECORD", -3: "KVREC_ERR_BLOCK_SIZE",
+    -4: "KVREC_ERR_PAGE_STRIDE", -5: "KVREC_ERR_ALIGNMENT", -6: "KVREC_ERR_SIZE",
+    -7: "KVREC_ERR_HIP",
+}
+EXPORTED_SYMBOLS = ("kvrec_page_stride", "kvrec_insert", "kvrec_gather", "kvrec_status_str")
+
+
+class KvrecError(RuntimeError):
+    """A non-zero kvrec_status returned by the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class kvrec_cache(ctypes.Structure):
+    _fields_ = [
+        ("base", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int64),
+        ("page_stride", ctypes.c_int64),
+        ("block_size", ctypes.c_int32),
+        ("record", ctypes.c_int32),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load ``libkvrec.so`` (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m quantized_paged_kv_rope_amd.build` "
+            "(or __graft_entry__.build()). There is no fallback path.")
+    L = ctypes.CDLL(path)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.kvrec_page_stride.argtypes = [i32, i32, ctypes.POINTER(i64)]
+    L.kvrec_page_stride.restype = ctypes.c_int
+    L.kvrec_insert.argtypes = [p, i64, ctypes.POINTER(kvrec_cache), p, p, p, i64, i32, i32, p]
+    L.kvrec_insert.restype = ctypes.c_int
+    L.kvrec_gather.argtypes = [ctypes.POINTER(kvrec_cache), p, i64, p, p]
+    L.kvrec_gather.restype = ctypes.c_int
+    L.kvrec_status_str.argtypes = [ctypes.c_int]
+    L.kvrec_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def kvrec_status_str(status: int) -> str:
+    return load_library().kvrec_status_str(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != KVREC_OK:
+        raise KvrecError(status, kvrec_status_str(status))
+
+
+def kvrec_page_stride(record: int, block_size: int) -> int:
+    out = ctypes.c_int64(0)
+    _check(load_library().kvrec_page_stride(record, block_size, ctypes.byref(out)))
+    return out.value
+
+
+def _require_gpu(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+
+
+def cache_descriptor(k_cache: torch.Tensor) -> kvrec_cache:
+    """The C descriptor of a ``[num_blocks, block_size, record]`` uint8 view."""
+    _require_gpu(k_cache, "k_cache")
+    if k_cache.dtype != torch.uint8 or k_cache.dim() != 3:
+        raise TypeError("k_cache must be a 3-D uint8 tensor [num_blocks, block_size, record]")
+    nb, bs, rec = k_cache.shape
+    if k_cache.stride(2) != 1 or (bs > 1 and k_cache.stride(1) != rec):
+        raise ValueError("k_cache must have stride(2) == 1 and stride(1) == record")
+    stride0 = k_cache.stride(0) if nb > 1 else kvrec_page_stride(rec, bs) if rec in (
+        RECORD_MXFP8, RECORD_LEGACY) else bs * rec
+    return kvrec_cache(k_cache.data_ptr(), nb, stride0, bs, rec)
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def kvrec_insert(kv: torch.Tensor, k_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                 positions: torch.Tensor, cos_sin_cache: torch.Tensor, block_size: int,
+                 record: Optional[int] = None) -> None:
+    """Fused RoPE + quantise + paged insert, in place on ``k_cache``.
+
+    Runs asynchronously on the current stream of ``kv``'s device."""
+    for name, t in (("kv", kv), ("slot_mapping", slot_mapping), ("positions", positions),
+                    ("cos_sin_cache", cos_sin_cache)):
+        _require_gpu(t, name)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if kv.dtype != torch.bfloat16 or kv.dim() != 2 or kv.shape[1] != HEAD_DIM:
+        raise TypeError("kv must be bf16 [tokens, 512]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1:
+        raise TypeError("slot_mapping must be a 1-D int64 tensor")
+    if positions.dtype != torch.int64 or positions.dim() != 1:
+        raise TypeError("positions must be a 1-D int64 tensor")
+    if cos_sin_cache.dtype != torch.float32 or cos_sin_cache.dim() != 2 or \
+            cos_sin_cache.shape[1] != ROPE_DIM:
+        raise TypeError("cos_sin_cache must be fp32 [max_pos, 64]")
+    n = slot_mapping.shape[0]
+    if kv.shape[0] < n or positions.shape[0] < n:
+        raise ValueError("kv and positions must cover every token of slot_mapping")
+    devs = {t.device for t in (kv, k_cache, slot_mapping, positions, cos_sin_cache)}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one device, got {devs}")
+    desc = cache_descriptor(k_cache)
+    rec = int(k_cache.shape[2]) if record is None else int(record)
+    with torch.cuda.device(kv.device):
+        _check(load_library().kvrec_insert(
+            kv.data_ptr(), n, ctypes.byref(desc), slot_mapping.data_ptr(), positions.data_ptr(),
+            cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], int(block_size), rec,
+            _stream_handle(kv.device)))
+
+
+def kvrec_gather(k_cache: torch.Tensor, token_indices: torch.Tensor,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged dequantise-and-gather: bf16 ``[*token_indices.shape, 512]``."""
+    _require_gpu(token_indices, "token_indices")
+    if token_indices.dtype != torch.int32 or not token_indices.is_contiguous():
+        raise TypeError("token_indices must be a contiguous int32 tensor")
+    desc = cache_descriptor(k_cache)
+    if token_indices.device != k_cache.device:
+        raise ValueError("token_indices and k_cache must be on one device")
+    shape = tuple(token_indices.shape) + (HEAD_DIM,)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=k_cache.device)
+    else:
+        _require_gpu(out, "out")
+        if out.dtype != torch.bfloat16 or tuple(out.shape) != shape or not out.is_contiguous():
+            raise ValueError(f"out must be contiguous bf16 {shape}")
+        if out.device != k_cache.device:
+            raise ValueError("out and k_cache must be on one device")
+    with torch.cuda.device(k_cache.device):
+        _check(load_library().kvrec_gather(
+            ctypes.byref(desc), token_indices.data_ptr(), token_indices.numel(), out.data_ptr(),
+            _stream_handle(k_cache.device)))
+    return out
+
+
+def alloc_cache(num_blocks: int, block_size: int, record: int,
+                page_stride: Optional[int] = None, device="cuda",
+                backing: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Allocate (or wrap) a flat uint8 backing and return ``(backing,
+    k_cache)`` where ``k_cache`` is the ``[num_blocks, block_size, record]``
+    view whose ``stride(0)`` is the page stride (default: block_size * record
+    rounded up to the record's alignment)."""
+    if page_stride is None:
+        page_stride = kvrec_page_stride(record, block_size)
+    nbytes = num_blocks * page_stride
+    if backing is None:
+        backing = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    elif backing.dtype != torch.uint8 or backing.dim() != 1 or backing.numel() < nbytes:
+        raise ValueError("backing must be a flat uint8 tensor of at least num_blocks*page_stride")
+    view = backing.as_strided((num_blocks, block_size, record), (page_stride, record, 1))
+    return backing, view

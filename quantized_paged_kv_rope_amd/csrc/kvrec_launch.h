@@ -1,0 +1,29 @@
+// kvrec_launch.h - internal interface between the C ABI (kvrec_api.cpp) and
+// the gfx950 kernels (kvrec_kernels.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvrec {
+
+// Geometry of a validated cache (all checks done on the host).
+struct CacheGeom {
+  uint8_t *base;
+  int64_t page_stride;
+  uint32_t block_size;
+  uint32_t total_slots;  // num_blocks * block_size, <= INT32_MAX
+};
+
+hipError_t launch_insert_mxfp8(const void *kv, int64_t n, const CacheGeom &g,
+                               const int64_t *slots, const int64_t *positions,
+                               const float *cos_sin, int64_t max_pos, hipStream_t stream);
+hipError_t launch_insert_legacy(const void *kv, int64_t n, const CacheGeom &g,
+                                const int64_t *slots, const int64_t *positions,
+                                const float *cos_sin, int64_t max_pos, hipStream_t stream);
+hipError_t launch_gather_mxfp8(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
+                               hipStream_t stream);
+hipError_t launch_gather_legacy(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
+                                hipStream_t stream);
+
+}  // namespace kvrec

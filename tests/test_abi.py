@@ -1,0 +1,183 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kvrec.h declares, rejects every malformed call on the host before any
+launch, and its kernels contain no fused multiply-add and no packed fp32 ops.
+
+Pointers passed here are fake but aligned addresses: every call below either
+fails validation or has nothing to launch (zero tokens), so the library never
+dereferences them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from quantized_paged_kv_rope_amd import binding as B
+from quantized_paged_kv_rope_amd import build as KB
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvrec.h")
+
+OK, NULL, RECORD, BLOCK, STRIDE, ALIGN, SIZE = 0, -1, -2, -3, -4, -5, -6
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH) or os.path.getmtime(B.LIB_PATH) < max(
+            os.path.getmtime(os.path.join(KB.CSRC, s)) for s in os.listdir(KB.CSRC)):
+        KB.build()
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvrec_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(B.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_library_does_not_depend_on_the_oracle():
+    needed = subprocess.run(["readelf", "-d", B.LIB_PATH], capture_output=True, text=True,
+                            check=True).stdout
+    assert "oracle" not in needed
+    pkg = os.path.dirname(B.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", src, re.M), f
+                assert "kvrec_oracle" not in src and "liboracle" not in src, f
+
+
+def test_status_strings(lib):
+    for code in (OK, NULL, RECORD, BLOCK, STRIDE, ALIGN, SIZE, -7, 12345):
+        s = lib.kvrec_status_str(code)
+        assert s and isinstance(s, bytes)
+    assert lib.kvrec_status_str(OK) == b"ok"
+
+
+@pytest.mark.parametrize("record,bs,want", [
+    (528, 32, 16896), (528, 64, 33792), (528, 128, 67584), (528, 256, 135168),
+    (584, 32, 19008), (584, 64, 37440), (584, 128, 74880), (584, 256, 149760),
+    (528, 1, 1024), (528, 4, 2560), (584, 4, 2880), (584, 1, 1152)])
+def test_page_stride(lib, record, bs, want):
+    out = ctypes.c_int64(-1)
+    assert lib.kvrec_page_stride(record, bs, ctypes.byref(out)) == OK
+    assert out.value == want
+
+
+def test_page_stride_errors(lib):
+    out = ctypes.c_int64(-1)
+    assert lib.kvrec_page_stride(528, 64, None) == NULL
+    assert lib.kvrec_page_stride(512, 64, ctypes.byref(out)) == RECORD
+    assert lib.kvrec_page_stride(576, 64, ctypes.byref(out)) == RECORD
+    assert lib.kvrec_page_stride(528, 0, ctypes.byref(out)) == BLOCK
+    assert out.value == -1
+
+
+def cache(base=FAKE, nb=4, stride=33792, bs=64, rec=528):
+    return B.kvrec_cache(base, nb, stride, bs, rec)
+
+
+def ins(lib, c, n=8, kv=FAKE, slots=FAKE, pos=FAKE, cs=FAKE, max_pos=16, bs=64, rec=528):
+    return lib.kvrec_insert(kv, n, ctypes.byref(c) if c is not None else None, slots, pos, cs,
+                            max_pos, bs, rec, None)
+
+
+def gat(lib, c, n=8, idx=FAKE, out=FAKE):
+    return lib.kvrec_gather(ctypes.byref(c) if c is not None else None, idx, n, out, None)
+
+
+def test_insert_validation(lib):
+    good = cache()
+    assert ins(lib, good, n=0) == OK                        # nothing to launch
+    assert ins(lib, good, n=0, kv=None, slots=None, pos=None, cs=None) == OK
+    assert ins(lib, None) == NULL
+    assert ins(lib, cache(base=None)) == NULL
+    assert ins(lib, good, kv=None) == NULL
+    assert ins(lib, good, slots=None) == NULL
+    assert ins(lib, good, pos=None) == NULL
+    assert ins(lib, good, cs=None) == NULL
+    assert ins(lib, good, rec=512) == RECORD
+    assert ins(lib, good, rec=584) == RECORD                 # != cache record
+    assert ins(lib, cache(rec=600, stride=38400), rec=600) == RECORD
+    assert ins(lib, good, bs=32) == BLOCK                    # != cache block size
+    assert ins(lib, cache(bs=0), bs=0) == BLOCK
+    assert ins(lib, cache(stride=33792 - 512)) == STRIDE    # < block_size * record
+    assert ins(lib, cache(stride=33792 + 64)) == STRIDE     # not a multiple of 512
+    assert ins(lib, cache(stride=212160)) == STRIDE         # the pages' bad block stride
+    assert ins(lib, cache(rec=584, stride=37440 + 512), rec=584) == STRIDE
+    assert ins(lib, cache(nb=-1)) == SIZE
+    assert ins(lib, cache(nb=2 ** 31 // 64)) == SIZE        # slots beyond int32
+    assert ins(lib, good, n=-1) == SIZE
+    assert ins(lib, good, n=2 ** 31) == SIZE
+    assert ins(lib, good, max_pos=0) == SIZE
+    assert ins(lib, cache(base=FAKE + 8)) == ALIGN
+    assert ins(lib, good, kv=FAKE + 8) == ALIGN
+    assert ins(lib, good, cs=FAKE + 4) == ALIGN
+    assert ins(lib, good, slots=FAKE + 4) == ALIGN
+    assert ins(lib, good, pos=FAKE + 4) == ALIGN
+
+
+def test_gather_validation(lib):
+    good = cache()
+    assert gat(lib, good, n=0) == OK
+    assert gat(lib, good, n=0, idx=None, out=None) == OK
+    assert gat(lib, None) == NULL
+    assert gat(lib, cache(base=None)) == NULL
+    assert gat(lib, good, idx=None) == NULL
+    assert gat(lib, good, out=None) == NULL
+    assert gat(lib, cache(rec=512)) == RECORD
+    assert gat(lib, cache(bs=0)) == BLOCK
+    assert gat(lib, cache(stride=1000)) == STRIDE
+    assert gat(lib, cache(rec=584, stride=37440 + 64)) == STRIDE
+    assert gat(lib, good, n=-3) == SIZE
+    assert gat(lib, good, out=FAKE + 8) == ALIGN
+    assert gat(lib, good, idx=FAKE + 2) == ALIGN
+    assert gat(lib, cache(base=FAKE + 1)) == ALIGN
+
+
+def test_legacy_cache_accepted(lib):
+    assert ins(lib, cache(rec=584, stride=37440), n=0, rec=584) == OK
+    assert gat(lib, cache(rec=584, stride=37440), n=0) == OK
+    assert gat(lib, cache(rec=584, stride=37440 + 576 * 3), n=0) == OK  # padded stride
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    kv = torch.zeros(4, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        B.kvrec_insert(kv, torch.zeros(1, 4, 528, dtype=torch.uint8), torch.zeros(4, dtype=torch.int64),
+                       torch.zeros(4, dtype=torch.int64), torch.zeros(8, 64), 4)
+    with pytest.raises(ValueError):
+        B.kvrec_gather(torch.zeros(1, 4, 528, dtype=torch.uint8), torch.zeros(4, dtype=torch.int32))
+
+
+def test_kernels_have_no_fma_and_no_packed_fp32():
+    asm = KB.device_asm()
+    code = "\n".join(l for l in asm.splitlines() if not l.lstrip().startswith((";", ".")))
+    for op in ("v_fma_f32", "v_fmac_f32", "v_mad_f32", "v_mac_f32", "v_fma_mix",
+               "v_pk_fma_f32", "v_pk_mul_f32", "v_pk_add_f32"):
+        assert op not in code, op
+    # fp32 denormals preserved for every kernel (mode 3 = keep inputs and outputs)
+    modes = re.findall(r"\.amdhsa_float_denorm_mode_32\s+(\d+)", asm)
+    assert modes and set(modes) == {"3"}
+    for needed in ("v_cvt_pk_fp8_f32", "v_cvt_pk_f32_fp8", "v_ldexp_f32", "ds_swizzle_b32"):
+        assert needed in code, needed
