@@ -1,0 +1,226 @@
+"""Benchmark of the paged KV-record codec on one MI355X.
+
+One step = the whole path over one batch: kvrec_insert of 262144 contiguous
+prefill tokens into the 528 B MXFP8 record (RoPE + quantise + paged store),
+then kvrec_gather of all 262144 slots back to bf16 (the round trip). Inputs
+are seeded synthetic data, resident in HBM before the timed region.
+
+Prints ONE JSON line: tokens/s through the path, per-kernel durations from
+HIP events recorded on the stream the kernels run on, the dominant kernel's
+achieved bandwidth against the 8 TB/s HBM peak, and the CPU oracle timed on
+a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+TOKENS = 262144
+# Algorithmic bytes per token (what the method must move):
+#   insert: kv 1024 + slot 8 + position 8 + cos/sin row 256 + record 528
+#   gather: index 4 + record 528 + bf16 row 1024
+INSERT_BYTES_PER_TOKEN = 1024 + 8 + 8 + 256 + 528
+GATHER_BYTES_PER_ROW = 4 + 528 + 1024
+PROFILE_PMC = os.path.join(ROOT, "profiles", "insert_mxfp8_prefill_262144_pmc.txt")
+KERNEL_SRC = os.path.join(ROOT, "quantized_paged_kv_rope_amd", "csrc", "kvrec_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per insert launch from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel source changed since."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    text = open(PROFILE_PMC).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(case, d_backing, d_out, sample: int):
+    """The oracle, as it stands, single-threaded on the host: insert and
+    gather of the first `sample` tokens of the workload. Also checks the GPU
+    result for those tokens (records and gathered rows) byte for byte."""
+    import oracle
+
+    oracle.lib()
+    n = sample
+    sub_blocks = (n + case.block_size - 1) // case.block_size
+    backing = np.zeros(sub_blocks * case.page_stride, np.uint8)
+    t0 = time.perf_counter()
+    oracle.insert(case.kv_bits[:n], backing, sub_blocks, case.page_stride, case.block_size,
+                  case.record, case.slot_mapping[:n], case.positions[:n], case.cos_sin)
+    out = oracle.gather(backing, sub_blocks, case.page_stride, case.block_size, case.record,
+                        case.gather_indices[:n])
+    dt = time.perf_counter() - t0
+    gpu_rec = d_backing[: sub_blocks * case.page_stride].cpu().numpy()
+    gpu_out = d_out[:n].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    exact = bool(np.array_equal(gpu_rec, backing) and np.array_equal(gpu_out, out))
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"insert + gather of the first {n} of the {case.num_tokens} tokens "
+                      f"(whole pages {sub_blocks}), single thread, {dt:.1f} s",
+            "seconds": round(dt, 3), "gpu_matches_oracle_on_sample": exact,
+            "host_cpu": _cpu_model(), "host_threads_available": os.cpu_count()}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=TOKENS)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the insert and gather "
+              "have no cross-GPU step; each GPU would run the same kernels on its own cache.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from quantized_paged_kv_rope_amd import binding as B
+    from quantized_paged_kv_rope_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.load_library()
+
+    case = W.prefill_262144(n=TOKENS)
+    kv = torch.from_numpy(case.kv_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    slots = torch.from_numpy(case.slot_mapping).to(dev)
+    pos = torch.from_numpy(case.positions).to(dev)
+    cos_sin = torch.from_numpy(case.cos_sin).to(dev)
+    idx = torch.from_numpy(case.gather_indices).to(dev)
+    backing, k_cache = B.alloc_cache(case.num_blocks, case.block_size, case.record,
+                                     case.page_stride, device=dev)
+    backing.zero_()
+    out = torch.empty((TOKENS, 512), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        B.kvrec_insert(kv, k_cache, slots, pos, cos_sin, case.block_size)
+        if ev is not None:
+            ev[1].record()
+        B.kvrec_gather(k_cache, idx, out=out)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ins_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    gat_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    ins_s, gat_s = ins_ms.mean() / 1e3, gat_ms.mean() / 1e3
+    ins_bytes = TOKENS * INSERT_BYTES_PER_TOKEN
+    gat_bytes = TOKENS * GATHER_BYTES_PER_ROW
+    ins_gbps = ins_bytes / ins_s / 1e9
+    gat_gbps = gat_bytes / gat_s / 1e9
+
+    copy_gbps = None
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * src.numel() * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9
+        del src, dst
+
+    traffic = counter_traffic()
+    result = {
+        "metric": "insert & gather tokens/s + achieved HBM GB/s vs MI355X peak (528B MXFP8)",
+        "value": TOKENS * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill_262144: insert 262144 contiguous tokens (positions 0.., slots "
+                        "0.., 4096 pages of 64) into the 528 B MXFP8 record, then gather all "
+                        "262144 slots back to bf16",
+            "tokens": TOKENS, "record_bytes": case.record, "block_size": case.block_size,
+            "page_stride": case.page_stride, "io": "bf16 in; e4m3 + UE8M0 record; bf16 out",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "insert_kernel (528 B MXFP8 record)",
+            "achieved": ins_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": ins_gbps / HBM_PEAK_GBPS, "traffic": traffic,
+            "algorithmic_bytes_per_launch": ins_bytes,
+        },
+        "kernels": {
+            "insert": {"avg_us": ins_s * 1e6, "p50_us": float(np.median(ins_ms)) * 1e3,
+                                    "GBps": ins_gbps, "frac_of_peak": ins_gbps / HBM_PEAK_GBPS,
+                                    "tokens_per_s": TOKENS / ins_s},
+            "gather": {"avg_us": gat_s * 1e6, "p50_us": float(np.median(gat_ms)) * 1e3,
+                                    "GBps": gat_gbps, "frac_of_peak": gat_gbps / HBM_PEAK_GBPS,
+                                    "tokens_per_s": TOKENS / gat_s,
+                                    "algorithmic_bytes_per_launch": gat_bytes},
+        },
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    if copy_gbps is not None:
+        result["device_copy_GBps"] = copy_gbps
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, backing, out, min(args.cpu_sample, TOKENS))
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

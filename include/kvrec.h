@@ -79,7 +79,7 @@ typedef enum kvrec_status {
  * s % block_size. */
 typedef struct kvrec_cache {
   void *base;          /* (device) byte 0 of page 0; 16-B aligned          */
-  int64_t num_blocks;  /* pages, >= 0                                      */
+  int64_t num_blocks;  /* pages, >= 0; num_blocks * block_size <= 2^30   */
   int64_t page_stride; /* bytes between pages; a multiple of 512 (528) or
                           576 (584) and >= block_size * record             */
   int32_t block_size;  /* tokens per page, >= 1                            */
@@ -101,7 +101,7 @@ int kvrec_page_stride(int32_t record, int32_t block_size, int64_t *page_stride_o
  *
  *   kv            (device) bf16 [num_tokens, 512], rows contiguous; 16-B
  *                 aligned; read only.
- *   num_tokens    >= 0, < 2^31; 0 returns KVREC_OK without a launch.
+ *   num_tokens    0 .. 2^30; 0 returns KVREC_OK without a launch.
  *   k_cache       host descriptor of the cache written in place.
  *   slot_mapping  (device) int64 [num_tokens]; 8-B aligned. A negative slot
  *                 skips its token: nothing is written for it.
@@ -136,7 +136,7 @@ int kvrec_insert(const void *kv, int64_t num_tokens, const kvrec_cache *k_cache,
  *   k_cache        host descriptor of the cache; read only.
  *   token_indices  (device) int32 [num_indices]; 4-B aligned. A negative
  *                  index gives a row of +0.
- *   num_indices    >= 0, < 2^31; 0 returns KVREC_OK without a launch.
+ *   num_indices    0 .. 2^30; 0 returns KVREC_OK without a launch.
  *   out            (device) bf16 [num_indices, 512]; 16-B aligned; written.
  *
  * Element d of a valid row is the bf16 nearest to e4m3fn(code_d) *

@@ -16,7 +16,8 @@
 
 namespace {
 
-constexpr int64_t kMaxCount = INT32_MAX;  // kernels index rows and slots in 32 bits
+constexpr int64_t kMaxCount = int64_t{1} << 30;  // rows and slots; keeps grids < 2^31 blocks
+constexpr int64_t kMaxPos = int64_t{1} << 31;    // cos/sin rows (a 512 GB table)
 
 bool misaligned(const void *p, uintptr_t align) {
   return (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0;
@@ -26,6 +27,18 @@ int64_t record_alignment(int32_t record) { return record == KVREC_RECORD_MXFP8 ?
 
 bool known_record(int32_t record) {
   return record == KVREC_RECORD_MXFP8 || record == KVREC_RECORD_LEGACY;
+}
+
+// Division by an invariant block size with a multiply-high (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, the quotient of
+// n by d is (umulhi(n, m) + n) >> l for every n < 2^31 (the sum cannot
+// overflow 32 bits there).
+void division_magic(uint32_t d, uint32_t *magic, uint32_t *shift) {
+  uint32_t l = 0;
+  while ((uint64_t{1} << l) < d) ++l;
+  *magic = static_cast<uint32_t>(((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1);
+  *shift = l;
 }
 
 // Checks a cache descriptor; on success fills the kernels' geometry.
@@ -44,6 +57,7 @@ int check_cache(const kvrec_cache *c, kvrec::CacheGeom *g) {
   g->page_stride = c->page_stride;
   g->block_size = static_cast<uint32_t>(c->block_size);
   g->total_slots = static_cast<uint32_t>(c->num_blocks * c->block_size);
+  division_magic(g->block_size, &g->div_magic, &g->div_shift);
   return KVREC_OK;
 }
 
@@ -75,7 +89,7 @@ int kvrec_insert(const void *kv, int64_t num_tokens, const kvrec_cache *k_cache,
   if (num_tokens == 0) return KVREC_OK;
   if (kv == nullptr || slot_mapping == nullptr || positions == nullptr || cos_sin_cache == nullptr)
     return KVREC_ERR_NULL;
-  if (max_pos < 1 || max_pos > INT64_MAX / (KVREC_ROPE_DIM * 4)) return KVREC_ERR_SIZE;
+  if (max_pos < 1 || max_pos > kMaxPos) return KVREC_ERR_SIZE;
   if (misaligned(kv, 16) || misaligned(cos_sin_cache, 16) || misaligned(slot_mapping, 8) ||
       misaligned(positions, 8))
     return KVREC_ERR_ALIGNMENT;

@@ -14,62 +14,127 @@
 // contraction here and no matrix core is used. One wave64 owns one token
 // (the lesson of [KV-only op] 实现拆解 5: with no query heads to iterate,
 // every wave must have a token of its own, or the launch idles most of the
-// chip). Lane l holds latent dims 8l..8l+7:
+// chip). On MI355X many short one-row waves also stream faster than fewer
+// waves that loop over rows. Lane l holds latent dims 8l..8l+7:
 //   - one 16 B global load per lane reads the 1 KB bf16 row, coalesced;
 //   - the 64 RoPE dims 448..511 sit in lanes 56..63, and the NeoX partner of
 //     dim 448+i is 480+i, i.e. lane l ^ 4: one ds_swizzle (xor 4) exchanges
 //     the raw words;
 //   - a 32-dim MXFP8 group is 4 adjacent lanes (a DPP quad), a 64-dim legacy
 //     group 8 lanes (quad + half-row mirror): amax needs 2 or 3 DPP steps;
-//   - the 8 codes of a lane are one 8 B store; the wave writes the 512 B data
-//     row contiguously, and the scale bytes as one 16-lane byte store.
+//   - the 8 codes of a lane are one 8 B store, so the wave writes the 512 B
+//     data row contiguously; the scale bytes are packed across lanes with DPP
+//     (or ds_bpermute) and written as dwords.
+// Latency. Every load that depends on nothing (the kv row, the slot, the
+// position) is issued at once; only the cos/sin row waits for the position.
+// The kv row is loaded before the slot is known, so a skipped token costs one
+// wasted 1 KB read but no serialised round trip. Streamed data uses
+// non-temporal loads and stores (it is touched once).
 //
 // Bit-exactness. Built with -ffp-contract=off (no FMA: the rotation is two
 // rounded products and one rounded add/subtract, in that order) and with fp32
-// denormals preserved. Scaling by 2^-e uses v_ldexp_f32 (exact, or one
-// rounding into the fp32 subnormal range, which e4m3 then rounds to +-0);
-// the e4m3fn conversion is v_cvt_pk_fp8_f32 (round to nearest even; inputs
-// never exceed 448 in magnitude because of how e is chosen).
+// denormals preserved. The encode is v_cvt_scalef32_pk_fp8_f32, which divides
+// by the power of two 2^e exactly and rounds once to e4m3fn (nearest even;
+// |r| * 2^-e never exceeds 448 because of how e is chosen); the decode is
+// v_cvt_scalef32_pk_bf16_fp8, which multiplies by 2^e and rounds once to bf16.
+// Both take the group's UE8M0 byte as the exponent field of their scale
+// operand, so no separate scaling instruction is needed.
 #include "kvrec_launch.h"
 
 namespace kvrec {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kBlockThreads = kWave * kWavesPerBlock;
 
 // DPP controls (gfx9 encoding).
-constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kHalfRowMirror = 0x141;  // lane i <-> 7-i within 8 lanes
+constexpr int kRowShl4 = 0x104;        // lane i reads lane i+4 of its 16-lane row
+constexpr int kRowShl8 = 0x108;
+constexpr int kRowShl12 = 0x10C;
 // ds_swizzle bit-mask mode: and 0x1F, or 0, xor 4 -> partner lane l ^ 4.
 constexpr int kSwizzleXor4 = 0x1F | (4 << 10);
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Cache policy of each stream, as a bit mask; a set bit makes that stream
+// non-temporal (touched once: do not keep it in L2 / Infinity Cache).
+enum : int {
+  kNtKv = 1,      // insert: bf16 rows
+  kNtTable = 2,   // insert: cos/sin rows
+  kNtData = 4,    // insert: record data rows
+  kNtScale = 8,   // insert: record scale rows
+  kNtRecord = 1,  // gather: record loads
+  kNtOut = 2,     // gather: bf16 rows
+};
+
+template <bool NT, typename T>
+__device__ __forceinline__ T ld(const T *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT, typename T>
+__device__ __forceinline__ void st(T *p, T v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// Counts (n <= 2^30), slots (< 2^30) and positions (max_pos <= 2^31) are
+// validated on the host to fit 32 bits, so the kernels index with 32-bit
+// scalar arithmetic.
 struct InsertArgs {
-  const uint4 *kv;  // [n, 64] x 16 B (bf16 [n, 512])
-  int64_t n;
-  uint8_t *base;
-  int64_t page_stride;
-  uint32_t block_size;
-  uint32_t total_slots;
+  const u32x4 *kv;  // [n, 64] x 16 B (bf16 [n, 512])
   const int64_t *slots;
   const int64_t *positions;
-  const float4 *cos_sin;  // [max_pos, 16] x 16 B (fp32 [max_pos, 64])
-  int64_t max_pos;
+  const f32x4 *cos_sin;  // [max_pos, 16] x 16 B (fp32 [max_pos, 64])
+  uint8_t *base;
+  int64_t page_stride;
+  uint32_t n;
+  uint32_t block_size;
+  uint32_t total_slots;
+  uint32_t div_magic;
+  uint32_t div_shift;
+  uint32_t max_pos;
 };
 
 struct GatherArgs {
+  const int32_t *indices;
+  u32x4 *out;  // [n, 64] x 16 B (bf16 [n, 512])
   const uint8_t *base;
   int64_t page_stride;
+  uint32_t n;
   uint32_t block_size;
   uint32_t total_slots;
-  const int32_t *indices;
-  int64_t n;
-  uint4 *out;  // [n, 64] x 16 B (bf16 [n, 512])
+  uint32_t div_magic;
+  uint32_t div_shift;
 };
 
-__device__ __forceinline__ void unpack_bf16x8(const uint4 &w, float f[8]) {
+// Page and offset of a slot (< 2^31) by the host's magic-number division.
+struct PageOff {
+  uint32_t page;
+  uint32_t off;
+};
+
+__device__ __forceinline__ PageOff page_of(uint32_t slot, uint32_t bs, uint32_t magic,
+                                           uint32_t shift) {
+  const uint32_t q = (__umulhi(slot, magic) + slot) >> shift;
+  return PageOff{q, slot - q * bs};
+}
+
+// v < limit for a 64-bit value read from memory, in 32-bit halves (negative
+// values have a non-zero high word).
+__device__ __forceinline__ bool below(int64_t v, uint32_t limit) {
+  return (static_cast<uint64_t>(v) >> 32) == 0 && static_cast<uint32_t>(v) < limit;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const u32x4 w, float f[8]) {
   f[0] = __uint_as_float(w.x << 16);
   f[1] = __uint_as_float(w.x & 0xFFFF0000u);
   f[2] = __uint_as_float(w.y << 16);
@@ -91,18 +156,41 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(v), Ctrl, 0xF, 0xF, true));
+}
+
+template <int Ctrl>
 __device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
-  return max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), Ctrl, 0xF,
-                                                                0xF, false)));
+  return max(v, dpp<Ctrl>(v));
+}
+
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int src_lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src_lane << 2, static_cast<int>(v)));
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD
+// b % 8), and each XCD has its own L2. Renumbering blocks so that XCD x owns
+// the contiguous range [x * G/8, (x+1) * G/8) keeps the small per-token
+// arrays (slots, positions, indices: 16..32 tokens per 128 B line) and the
+// 16 B scale rows of neighbouring tokens in one L2 instead of eight. The grid
+// is padded to a multiple of 8 blocks; the padding blocks find no work.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int64_t xcd_block() {
+  const uint32_t b = blockIdx.x;
+  const uint32_t per_xcd = gridDim.x / kXcds;
+  return static_cast<int64_t>(b % kXcds) * per_xcd + b / kXcds;
 }
 
 // Largest |x| of this lane's 8 values, as fp32 bits (compares as unsigned
 // integers because every value is finite and non-negative).
 __device__ __forceinline__ uint32_t lane_amax_bits(const float f[8]) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(f[k]) & 0x7FFFFFFFu);
-  return m;
+  float m = fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fabsf(f[2]));
+  m = fmaxf(fmaxf(m, fabsf(f[3])), fabsf(f[4]));
+  m = fmaxf(fmaxf(m, fabsf(f[5])), fabsf(f[6]));
+  return __float_as_uint(fmaxf(m, fabsf(f[7])));
 }
 
 // UE8M0 exponent of a group ([MXFP8 record] 关键源码片段: ceil(log2(amax/448))):
@@ -116,17 +204,25 @@ __device__ __forceinline__ int scale_exponent(uint32_t amax_bits) {
   return e < -127 ? -127 : e;  // finite input keeps e <= 120, far below +127
 }
 
-// e4m3fn codes of r * 2^-e for 8 values, byte k = value k.
-__device__ __forceinline__ uint2 encode_e4m3x8(const float f[8], int e) {
-  const int ne = -e;
-  float y[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) y[k] = __builtin_amdgcn_ldexpf(f[k], ne);
-  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
-  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
-  return make_uint2(static_cast<uint32_t>(w0), static_cast<uint32_t>(w1));
+// The gfx950 scaled conversions read only the exponent field of their fp32
+// scale operand, which is exactly a UE8M0 byte: scale = byte << 23 stands for
+// 2^(byte - 127). v_cvt_scalef32_pk_fp8_f32 gives e4m3fn(x / 2^(byte-127))
+// rounded to nearest even (the division by a power of two is exact, so this
+// is one rounding of the exact r * 2^-e); v_cvt_scalef32_pk_bf16_fp8 gives
+// bf16(e4m3fn(code) * 2^(byte-127)).
+__device__ __forceinline__ float e8m0_as_f32(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// e4m3fn codes of r * 2^-e for 8 values (scale byte = e + 127), byte k = value k.
+__device__ __forceinline__ u32x2 encode_e4m3x8(const float f[8], uint32_t scale_byte) {
+  const float sc = e8m0_as_f32(scale_byte);
+  // The first conversion of each word writes its low half and keeps the high
+  // half of `old`, which the second one then overwrites: any old value works.
+  const s16x2 any = __builtin_bit_cast(s16x2, sc);
+  s16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(any, f[0], f[1], sc, false);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, f[2], f[3], sc, true);
+  s16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(any, f[4], f[5], sc, false);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, f[6], f[7], sc, true);
+  return u32x2{__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1)};
 }
 
 // Rotate the tail dims held by lanes 56..63 in place. All lanes must call it
@@ -134,9 +230,9 @@ __device__ __forceinline__ uint2 encode_e4m3x8(const float f[8], int e) {
 //   lanes 56..59 hold x1 = dims 448+i, lanes 60..63 hold x2 = dims 480+i,
 //   i = 8*(lane & 3) + k; cos = row[i], sin = row[32 + i].
 //   r1 = x1*c - x2*s,  r2 = x2*c + x1*s  (each operation rounded separately)
-__device__ __forceinline__ void rope_tail(float f[8], const uint4 &raw, int lane,
-                                          const float4 *row) {
-  uint4 pr;
+__device__ __forceinline__ void rope_tail(float f[8], const u32x4 raw, int lane, const f32x4 c0,
+                                          const f32x4 c1, const f32x4 s0, const f32x4 s1) {
+  u32x4 pr;
   pr.x = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(raw.x), kSwizzleXor4));
   pr.y = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(raw.y), kSwizzleXor4));
   pr.z = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(raw.z), kSwizzleXor4));
@@ -144,9 +240,6 @@ __device__ __forceinline__ void rope_tail(float f[8], const uint4 &raw, int lane
   if (lane >= 56) {
     float g[8];
     unpack_bf16x8(pr, g);
-    const int q = 2 * (lane & 3);  // float4 index of cos[8*(lane&3)]
-    const float4 c0 = row[q], c1 = row[q + 1];
-    const float4 s0 = row[8 + q], s1 = row[9 + q];
     const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
     const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
     const bool second = (lane & 4) != 0;  // this lane holds x2 (dims 480..)
@@ -159,185 +252,240 @@ __device__ __forceinline__ void rope_tail(float f[8], const uint4 &raw, int lane
   }
 }
 
-// Shared front half of both inserts: returns false if the wave's token is
-// skipped; otherwise fills the rotated values and the page/offset.
-struct TokenSlot {
-  uint8_t *page;
-  uint32_t off;
-};
-
-__device__ __forceinline__ bool load_rotated(const InsertArgs &a, int64_t t, int lane, float f[8],
-                                             TokenSlot &ts) {
-  const int64_t slot = a.slots[t];
-  if (slot < 0 || slot >= static_cast<int64_t>(a.total_slots)) return false;
-  const int64_t pos = a.positions[t];
-  if (pos < 0 || pos >= a.max_pos) return false;
-  const uint4 raw = a.kv[t * kWave + lane];
+// Encode one loaded token and store its record. `raw` is the lane's 16 B of
+// the bf16 row, c0..s1 the lane's cos/sin values (lanes 56..63 only).
+template <int P, bool kLegacy>
+__device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, const u32x4 raw,
+                                             const f32x4 c0, const f32x4 c1, const f32x4 s0,
+                                             const f32x4 s1, uint32_t slot) {
+  float f[8];
   unpack_bf16x8(raw, f);
-  rope_tail(f, raw, lane, a.cos_sin + pos * 16);
-  const uint32_t s = static_cast<uint32_t>(slot);
-  const uint32_t pg = s / a.block_size;
-  ts.off = s - pg * a.block_size;
-  ts.page = a.base + static_cast<int64_t>(pg) * a.page_stride;
-  return true;
-}
-
-// MXFP8 record, 528 B: 512 codes at page + off*512, 16 scale bytes at
-// page + block_size*512 + off*16 ([MXFP8 record] 功能与动机, 关键源码片段).
-__global__ __launch_bounds__(kBlockThreads) void insert_mxfp8_kernel(const InsertArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
-  if (t >= a.n) return;
-  float f[8];
-  TokenSlot ts;
-  if (!load_rotated(a, t, lane, f, ts)) return;
+  rope_tail(f, raw, lane, c0, c1, s0, s1);
+  const PageOff po = page_of(slot, a.block_size, a.div_magic, a.div_shift);
+  const uint32_t off = po.off;
+  uint8_t *page = a.base + static_cast<int64_t>(po.page) * a.page_stride;
+  constexpr bool nt_data = (P & kNtData) != 0;
+  constexpr bool nt_scale = (P & kNtScale) != 0;
 
   uint32_t amax = lane_amax_bits(f);
   amax = dpp_umax<kQuadXor1>(amax);
   amax = dpp_umax<kQuadXor2>(amax);
+  if constexpr (kLegacy) amax = dpp_umax<kHalfRowMirror>(amax);  // 8 lanes = 64 dims
   const int e = scale_exponent(amax);
+  const uint32_t b = static_cast<uint32_t>(e + 127);
 
-  const uint2 codes = encode_e4m3x8(f, e);
-  *reinterpret_cast<uint2 *>(ts.page + ts.off * 512u + lane * 8) = codes;
-  if ((lane & 3) == 0)
-    ts.page[a.block_size * 512u + ts.off * 16u + (lane >> 2)] = static_cast<uint8_t>(e + 127);
-}
-
-// Legacy record, 584 B: a 576 B data row (448 codes of dims 0..447, then the
-// 64 rotated tail dims as little-endian bf16) at page + off*576, and an 8 B
-// scale row (7 scales over 64-dim groups, then a 0 pad byte) at
-// page + block_size*576 + off*8 ([MXFP8 record] 功能与动机).
-__global__ __launch_bounds__(kBlockThreads) void insert_legacy_kernel(const InsertArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
-  if (t >= a.n) return;
-  float f[8];
-  TokenSlot ts;
-  if (!load_rotated(a, t, lane, f, ts)) return;
-
-  uint32_t amax = lane_amax_bits(f);
-  amax = dpp_umax<kQuadXor1>(amax);
-  amax = dpp_umax<kQuadXor2>(amax);
-  amax = dpp_umax<kHalfRowMirror>(amax);  // 8 lanes = 64 dims
-  const int e = scale_exponent(amax);
-
-  uint8_t *row = ts.page + ts.off * 576u;
-  uint8_t *srow = ts.page + a.block_size * 576u + ts.off * 8u;
-  if (lane < 56) {
-    *reinterpret_cast<uint2 *>(row + lane * 8) = encode_e4m3x8(f, e);
-    if ((lane & 7) == 0) srow[lane >> 3] = static_cast<uint8_t>(e + 127);
+  if constexpr (!kLegacy) {
+    // MXFP8 record, 528 B: 512 codes at page + off*512, 16 scale bytes at
+    // page + block_size*512 + off*16 ([MXFP8 record] 功能与动机, 关键源码片段).
+    st<nt_data>(reinterpret_cast<u32x2 *>(page + off * 512u + lane * 8), encode_e4m3x8(f, b));
+    // Scale byte of group g lives in lanes 4g..4g+3; lane 16k gathers groups
+    // 4k..4k+3 from lanes 16k, 16k+4, 16k+8, 16k+12 and stores them as a dword.
+    const uint32_t word =
+        b | (dpp<kRowShl4>(b) << 8) | (dpp<kRowShl8>(b) << 16) | (dpp<kRowShl12>(b) << 24);
+    if ((lane & 15) == 0)
+      st<nt_scale>(
+          reinterpret_cast<uint32_t *>(page + a.block_size * 512u + off * 16u + (lane >> 2)),
+          word);
   } else {
-    uint4 h;
-    h.x = pack_bf16x2(f[0], f[1]);
-    h.y = pack_bf16x2(f[2], f[3]);
-    h.z = pack_bf16x2(f[4], f[5]);
-    h.w = pack_bf16x2(f[6], f[7]);
-    *reinterpret_cast<uint4 *>(row + 448 + (lane - 56) * 16) = h;
-    if (lane == 56) srow[7] = 0;
+    // Legacy record, 584 B: a 576 B data row (448 codes of dims 0..447, then
+    // the 64 rotated tail dims as little-endian bf16) at page + off*576, and
+    // an 8 B scale row (7 scales over 64-dim groups, then a 0 pad byte) at
+    // page + block_size*576 + off*8 ([MXFP8 record] 功能与动机).
+    uint8_t *row = page + off * 576u;
+    if (lane < 56) {
+      st<nt_data>(reinterpret_cast<u32x2 *>(row + lane * 8), encode_e4m3x8(f, b));
+    } else {
+      u32x4 h;
+      h.x = pack_bf16x2(f[0], f[1]);
+      h.y = pack_bf16x2(f[2], f[3]);
+      h.z = pack_bf16x2(f[4], f[5]);
+      h.w = pack_bf16x2(f[6], f[7]);
+      st<nt_data>(reinterpret_cast<u32x4 *>(row + 448 + (lane - 56) * 16), h);
+    }
+    // Scale byte of group g lives in lanes 8g..8g+7. Lane 0 packs groups
+    // 0..3 (lanes 0, 8, 16, 24), lane 32 packs groups 4..6 and the pad byte.
+    const uint32_t b1 = lane_read(b, (lane + 8) & 63);
+    const uint32_t b2 = lane_read(b, (lane + 16) & 63);
+    const uint32_t r3 = lane_read(b, (lane + 24) & 63);
+    const uint32_t b3 = lane == 32 ? 0u : r3;
+    const uint32_t word = b | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    if ((lane & 31) == 0)
+      st<nt_scale>(
+          reinterpret_cast<uint32_t *>(page + a.block_size * 576u + off * 8u + (lane >> 3)),
+          word);
   }
 }
 
-// bf16 of e4m3(code) * 2^e for 8 codes (exact products; the rounding only
-// matters for e <= -125).
-__device__ __forceinline__ uint4 decode_e4m3x8(const uint2 codes, int e) {
-  typedef float float2v __attribute__((ext_vector_type(2)));
-  const float2v a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes.x), false);
-  const float2v b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes.x), true);
-  const float2v c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes.y), false);
-  const float2v d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes.y), true);
-  uint4 o;
-  o.x = pack_bf16x2(__builtin_amdgcn_ldexpf(a.x, e), __builtin_amdgcn_ldexpf(a.y, e));
-  o.y = pack_bf16x2(__builtin_amdgcn_ldexpf(b.x, e), __builtin_amdgcn_ldexpf(b.y, e));
-  o.z = pack_bf16x2(__builtin_amdgcn_ldexpf(c.x, e), __builtin_amdgcn_ldexpf(c.y, e));
-  o.w = pack_bf16x2(__builtin_amdgcn_ldexpf(d.x, e), __builtin_amdgcn_ldexpf(d.y, e));
-  return o;
+// Insert: wave w of block b handles tokens T*(W*b + w) .. +T-1. For all of
+// them it first issues the loads that depend on nothing (kv rows, slots,
+// positions), then the cos/sin rows (which need the positions), and only
+// then encodes and stores. A token whose slot is negative (or out of range)
+// or whose position is out of range is skipped.
+template <int P, int W, int T, bool kLegacy>
+__global__ __launch_bounds__(W * kWave) void insert_kernel(const InsertArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t t0 = (static_cast<uint32_t>(xcd_block()) * W + wave) * T;
+  if (t0 >= a.n) return;
+
+  u32x4 raw[T];
+  uint32_t slot[T], pos[T];
+  bool ok[T];
+#pragma unroll
+  for (int k = 0; k < T; ++k) {
+    const uint32_t t = t0 + k;
+    const bool in = (T == 1) || t < a.n;
+    raw[k] = in ? ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t) * kWave + lane)
+                : u32x4{0, 0, 0, 0};
+    const int64_t sl = in ? a.slots[t] : -1;
+    const int64_t ps = in ? a.positions[t] : -1;
+    ok[k] = below(sl, a.total_slots) && below(ps, a.max_pos);
+    slot[k] = static_cast<uint32_t>(sl);
+    pos[k] = static_cast<uint32_t>(ps);
+  }
+  // Only lanes 56..63 read (and later use) the cos/sin values. The empty asm
+  // statements give the registers an unset value in the other lanes, so the
+  // compiler does not spend 16 moves per token zero-filling them.
+  f32x4 c0[T], c1[T], s0[T], s1[T];
+#pragma unroll
+  for (int k = 0; k < T; ++k) {
+    asm("" : "=v"(c0[k]), "=v"(c1[k]), "=v"(s0[k]), "=v"(s1[k]));
+    if (ok[k] && lane >= 56) {
+      const f32x4 *row = a.cos_sin + static_cast<uint64_t>(pos[k]) * 16;
+      const int q = 2 * (lane & 3);  // float4 index of cos[8*(lane&3)]
+      constexpr bool nt = (P & kNtTable) != 0;
+      c0[k] = ld<nt>(row + q);
+      c1[k] = ld<nt>(row + q + 1);
+      s0[k] = ld<nt>(row + 8 + q);
+      s1[k] = ld<nt>(row + 9 + q);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < T; ++k)
+    if (ok[k]) encode_store<P, kLegacy>(a, lane, raw[k], c0[k], c1[k], s0[k], s1[k], slot[k]);
+}
+
+// bf16 of e4m3fn(code) * 2^(scale_byte - 127) for 8 codes, value k = byte k.
+__device__ __forceinline__ u32x4 decode_e4m3x8(const u32x2 codes, uint32_t scale_byte) {
+  const float sc = e8m0_as_f32(scale_byte);
+  return u32x4{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, sc, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, sc, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, sc, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, sc, true))};
 }
 
 // Gather: index = page*block_size + offset; a negative (or out-of-range)
-// index gives a row of +0 ([FlashMLA]: -1 marks an invalid entry).
-__global__ __launch_bounds__(kBlockThreads) void gather_mxfp8_kernel(const GatherArgs a) {
+// index gives a row of +0 ([FlashMLA]: -1 marks an invalid entry). Each wave
+// handles kRows consecutive output rows: all index loads first, then all
+// record loads, then the decodes and stores.
+template <bool kLegacy, int kRows, int P, int W>
+__global__ __launch_bounds__(W * kWave) void gather_kernel(const GatherArgs a) {
+  constexpr bool NT = (P & kNtRecord) != 0;
+  constexpr uint32_t kRowBytes = kLegacy ? 576u : 512u;
+  constexpr uint32_t kScaleBytes = kLegacy ? 8u : 16u;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
-  if (j >= a.n) return;
-  uint4 *dst = a.out + j * kWave + lane;
-  const int32_t idx = a.indices[j];
-  if (idx < 0 || static_cast<uint32_t>(idx) >= a.total_slots) {
-    *dst = make_uint4(0, 0, 0, 0);
-    return;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t j0 = (static_cast<uint32_t>(xcd_block()) * W + wave) * kRows;
+  if (j0 >= a.n) return;
+
+  int32_t idx[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) idx[r] = (j0 + r < a.n) ? a.indices[j0 + r] : -1;
+
+  // Registers of rows (or lanes) that load nothing are left unset (empty asm)
+  // instead of zero-filled: those rows store zeros and never read them.
+  u32x2 codes[kRows];
+  uint32_t sbyte[kRows];
+  u32x4 tail[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    asm("" : "=v"(codes[r]), "=v"(sbyte[r]), "=v"(tail[r]));
+    if (static_cast<uint32_t>(idx[r]) < a.total_slots) {  // negative -> huge
+      const PageOff po =
+          page_of(static_cast<uint32_t>(idx[r]), a.block_size, a.div_magic, a.div_shift);
+      const uint32_t off = po.off;
+      const uint8_t *page = a.base + static_cast<int64_t>(po.page) * a.page_stride;
+      const uint8_t *row = page + off * kRowBytes;
+      const uint8_t *scales = page + a.block_size * kRowBytes + off * kScaleBytes;
+      if (!kLegacy || lane < 56) {
+        codes[r] = ld<NT>(reinterpret_cast<const u32x2 *>(row + lane * 8));
+        sbyte[r] = ld<NT>(scales + (kLegacy ? (lane >> 3) : (lane >> 2)));
+      } else {
+        tail[r] = ld<NT>(reinterpret_cast<const u32x4 *>(row + 448 + (lane - 56) * 16));
+      }
+    }
   }
-  const uint32_t s = static_cast<uint32_t>(idx);
-  const uint32_t pg = s / a.block_size;
-  const uint32_t off = s - pg * a.block_size;
-  const uint8_t *page = a.base + static_cast<int64_t>(pg) * a.page_stride;
-  const uint2 codes = *reinterpret_cast<const uint2 *>(page + off * 512u + lane * 8);
-  const int e = static_cast<int>(page[a.block_size * 512u + off * 16u + (lane >> 2)]) - 127;
-  *dst = decode_e4m3x8(codes, e);
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    if (j0 + r >= a.n) break;
+    u32x4 o = u32x4{0, 0, 0, 0};
+    if (static_cast<uint32_t>(idx[r]) < a.total_slots) {
+      if (!kLegacy || lane < 56)
+        o = decode_e4m3x8(codes[r], sbyte[r]);
+      else
+        o = tail[r];
+    }
+    st<(P & kNtOut) != 0>(a.out + static_cast<uint64_t>(j0 + r) * kWave + lane, o);
+  }
 }
 
-__global__ __launch_bounds__(kBlockThreads) void gather_legacy_kernel(const GatherArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
-  if (j >= a.n) return;
-  uint4 *dst = a.out + j * kWave + lane;
-  const int32_t idx = a.indices[j];
-  if (idx < 0 || static_cast<uint32_t>(idx) >= a.total_slots) {
-    *dst = make_uint4(0, 0, 0, 0);
-    return;
-  }
-  const uint32_t s = static_cast<uint32_t>(idx);
-  const uint32_t pg = s / a.block_size;
-  const uint32_t off = s - pg * a.block_size;
-  const uint8_t *page = a.base + static_cast<int64_t>(pg) * a.page_stride;
-  const uint8_t *row = page + off * 576u;
-  if (lane < 56) {
-    const uint2 codes = *reinterpret_cast<const uint2 *>(row + lane * 8);
-    const int e = static_cast<int>(page[a.block_size * 576u + off * 8u + (lane >> 3)]) - 127;
-    *dst = decode_e4m3x8(codes, e);
-  } else {
-    *dst = *reinterpret_cast<const uint4 *>(row + 448 + (lane - 56) * 16);
-  }
-}
+// Launch configuration, chosen by timing every combination on MI355X, both as
+// single launches after the caches were cleaned and as the back-to-back
+// insert -> gather step (prefill 262144, legacy 65536, decode 16384 and a
+// 131072-row top-k gather). The insert's streamed inputs (kv rows, cos/sin
+// rows) are non-temporal while its records are stored normally: they are read
+// back soon, and the partial lines of scattered slots merge in cache. The
+// gather's bf16 output is non-temporal: written once, and as large as the
+// Infinity Cache, it would otherwise evict the records. One wave per insert
+// block; two rows per gather wave, two waves per block.
+constexpr int kInsertPolicy = kNtKv | kNtTable;
+constexpr int kInsertWaves = 1;   // waves per block
+constexpr int kInsertTokens = 1;  // tokens per wave
+constexpr int kGatherPolicy = kNtOut;
+constexpr int kGatherWaves = 2;
+constexpr int kGatherRows = 2;    // rows per wave
 
-inline dim3 grid_for(int64_t n) {
-  return dim3(static_cast<unsigned>((n + kWavesPerBlock - 1) / kWavesPerBlock));
-}
-
-template <typename Args>
-hipError_t launch(void (*kernel)(const Args), const Args &a, int64_t n, hipStream_t stream) {
+// Launches `kernel` with blocks of W waves over `waves` waves; the grid is
+// padded to a whole number of blocks per XCD (see xcd_block).
+template <int W, typename Args>
+hipError_t launch(void (*kernel)(const Args), const Args &a, int64_t waves, hipStream_t stream) {
   void *params[] = {const_cast<Args *>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid_for(n), dim3(kBlockThreads),
-                         params, 0, stream);
+  const int64_t blocks = (waves + W - 1) / W;
+  const dim3 grid(static_cast<unsigned>((blocks + kXcds - 1) / kXcds * kXcds));
+  return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(W * kWave), params, 0,
+                         stream);
 }
 
 InsertArgs make_insert_args(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
                             const int64_t *positions, const float *cos_sin, int64_t max_pos) {
   InsertArgs a;
-  a.kv = static_cast<const uint4 *>(kv);
-  a.n = n;
-  a.base = g.base;
-  a.page_stride = g.page_stride;
-  a.block_size = g.block_size;
-  a.total_slots = g.total_slots;
+  a.kv = static_cast<const u32x4 *>(kv);
   a.slots = slots;
   a.positions = positions;
-  a.cos_sin = reinterpret_cast<const float4 *>(cos_sin);
-  a.max_pos = max_pos;
+  a.cos_sin = reinterpret_cast<const f32x4 *>(cos_sin);
+  a.base = g.base;
+  a.page_stride = g.page_stride;
+  a.n = static_cast<uint32_t>(n);
+  a.block_size = g.block_size;
+  a.total_slots = g.total_slots;
+  a.div_magic = g.div_magic;
+  a.div_shift = g.div_shift;
+  a.max_pos = static_cast<uint32_t>(max_pos);
   return a;
 }
 
 GatherArgs make_gather_args(const CacheGeom &g, const int32_t *indices, int64_t n, void *out) {
   GatherArgs a;
+  a.indices = indices;
+  a.out = static_cast<u32x4 *>(out);
   a.base = g.base;
   a.page_stride = g.page_stride;
+  a.n = static_cast<uint32_t>(n);
   a.block_size = g.block_size;
   a.total_slots = g.total_slots;
-  a.indices = indices;
-  a.n = n;
-  a.out = static_cast<uint4 *>(out);
+  a.div_magic = g.div_magic;
+  a.div_shift = g.div_shift;
   return a;
 }
 
@@ -346,25 +494,33 @@ GatherArgs make_gather_args(const CacheGeom &g, const int32_t *indices, int64_t 
 hipError_t launch_insert_mxfp8(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
                                const int64_t *positions, const float *cos_sin, int64_t max_pos,
                                hipStream_t stream) {
-  return launch(insert_mxfp8_kernel, make_insert_args(kv, n, g, slots, positions, cos_sin, max_pos),
-                n, stream);
+  return launch<kInsertWaves>(
+      insert_kernel<kInsertPolicy, kInsertWaves, kInsertTokens, false>,
+      make_insert_args(kv, n, g, slots, positions, cos_sin, max_pos),
+      (n + kInsertTokens - 1) / kInsertTokens, stream);
 }
 
 hipError_t launch_insert_legacy(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
                                 const int64_t *positions, const float *cos_sin, int64_t max_pos,
                                 hipStream_t stream) {
-  return launch(insert_legacy_kernel,
-                make_insert_args(kv, n, g, slots, positions, cos_sin, max_pos), n, stream);
+  return launch<kInsertWaves>(
+      insert_kernel<kInsertPolicy, kInsertWaves, kInsertTokens, true>,
+      make_insert_args(kv, n, g, slots, positions, cos_sin, max_pos),
+      (n + kInsertTokens - 1) / kInsertTokens, stream);
 }
 
 hipError_t launch_gather_mxfp8(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
                                hipStream_t stream) {
-  return launch(gather_mxfp8_kernel, make_gather_args(g, indices, n, out), n, stream);
+  return launch<kGatherWaves>(gather_kernel<false, kGatherRows, kGatherPolicy, kGatherWaves>,
+                              make_gather_args(g, indices, n, out),
+                              (n + kGatherRows - 1) / kGatherRows, stream);
 }
 
 hipError_t launch_gather_legacy(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
                                 hipStream_t stream) {
-  return launch(gather_legacy_kernel, make_gather_args(g, indices, n, out), n, stream);
+  return launch<kGatherWaves>(gather_kernel<true, kGatherRows, kGatherPolicy, kGatherWaves>,
+                              make_gather_args(g, indices, n, out),
+                              (n + kGatherRows - 1) / kGatherRows, stream);
 }
 
 }  // namespace kvrec

@@ -12,7 +12,9 @@ struct CacheGeom {
   uint8_t *base;
   int64_t page_stride;
   uint32_t block_size;
-  uint32_t total_slots;  // num_blocks * block_size, <= INT32_MAX
+  uint32_t total_slots;  // num_blocks * block_size, <= 2^30
+  uint32_t div_magic;    // slot / block_size == (umulhi(slot, div_magic) + slot) >> div_shift
+  uint32_t div_shift;    //   for every slot < 2^31
 };
 
 hipError_t launch_insert_mxfp8(const void *kv, int64_t n, const CacheGeom &g,

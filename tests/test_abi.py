@@ -124,9 +124,10 @@ def test_insert_validation(lib):
     assert ins(lib, cache(stride=212160)) == STRIDE         # the pages' bad block stride
     assert ins(lib, cache(rec=584, stride=37440 + 512), rec=584) == STRIDE
     assert ins(lib, cache(nb=-1)) == SIZE
-    assert ins(lib, cache(nb=2 ** 31 // 64)) == SIZE        # slots beyond int32
+    assert ins(lib, cache(nb=2 ** 30 // 64 + 1)) == SIZE    # more than 2^30 slots
+    assert ins(lib, cache(nb=2 ** 30 // 64), n=0) == OK
     assert ins(lib, good, n=-1) == SIZE
-    assert ins(lib, good, n=2 ** 31) == SIZE
+    assert ins(lib, good, n=2 ** 30 + 1) == SIZE
     assert ins(lib, good, max_pos=0) == SIZE
     assert ins(lib, cache(base=FAKE + 8)) == ALIGN
     assert ins(lib, good, kv=FAKE + 8) == ALIGN
@@ -179,5 +180,5 @@ def test_kernels_have_no_fma_and_no_packed_fp32():
     # fp32 denormals preserved for every kernel (mode 3 = keep inputs and outputs)
     modes = re.findall(r"\.amdhsa_float_denorm_mode_32\s+(\d+)", asm)
     assert modes and set(modes) == {"3"}
-    for needed in ("v_cvt_pk_fp8_f32", "v_cvt_pk_f32_fp8", "v_ldexp_f32", "ds_swizzle_b32"):
+    for needed in ("v_cvt_scalef32_pk_fp8_f32", "v_cvt_scalef32_pk_bf16_fp8", "ds_swizzle_b32"):
         assert needed in code, needed
