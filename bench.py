@@ -11,6 +11,12 @@ achieved bandwidth against the 8 TB/s HBM peak, and the CPU oracle timed on
 a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --all-configs     # adds a per-workload table on stderr
+
+The JSON line on stdout is the only headline. --all-configs also times each
+kernel on the other workloads (single launches after a 1 GiB read that
+leaves the caches clean, and back-to-back launches replayed from a HIP graph)
+and prints them as a table on stderr.
 """
 from __future__ import annotations
 
@@ -83,6 +89,104 @@ def cpu_baseline(case, d_backing, d_out, sample: int):
             "host_cpu": _cpu_model(), "host_threads_available": os.cpu_count()}
 
 
+def all_configs_report(dev, out=sys.stderr) -> list:
+    """Per-kernel timings of every workload (cold and back-to-back)."""
+    import torch
+
+    from quantized_paged_kv_rope_amd import binding as B
+    from quantized_paged_kv_rope_amd import workloads as W
+
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+
+    def cold(fn, reps=10):
+        fn()
+        ts = []
+        for _ in range(reps):
+            flush.sum(dtype=torch.int64)  # reads 1 GiB: caches left holding clean lines
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    def replayed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (5 * reps)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    rows = []
+
+    def add(workload, op, n, valid, nbytes, fn):
+        c, r = cold(fn), replayed(fn)
+        rows.append({"workload": workload, "op": op, "rows": n, "valid": valid,
+                     "algorithmic_bytes": nbytes, "cold_us": c, "replayed_us": r,
+                     "cold_GBps": nbytes / c / 1e3, "replayed_GBps": nbytes / r / 1e3,
+                     "tokens_per_s_replayed": n / r * 1e6})
+
+    cases = [W.mixed_1024(), W.decode_16384(), W.prefill_262144(), W.legacy_65536()]
+    for case in cases:
+        kv = up(case.kv_bits.view(np.int16)).view(torch.bfloat16)
+        sl, ps, cs = up(case.slot_mapping), up(case.positions), up(case.cos_sin)
+        backing, kc = B.alloc_cache(case.num_blocks, case.block_size, case.record,
+                                    case.page_stride, device=dev)
+        backing.zero_()
+        valid = int((case.slot_mapping >= 0).sum())
+        n = case.num_tokens
+        ib = valid * (1024 + 8 + 8 + 256 + case.record) + (n - valid) * 8
+        add(case.name, f"insert {case.record} B", n, valid, ib,
+            lambda: B.kvrec_insert(kv, kc, sl, ps, cs, case.block_size))
+        if case.name.startswith("decode"):
+            continue
+        idx = up(case.gather_indices)
+        o = torch.empty((idx.numel(), 512), dtype=torch.bfloat16, device=dev)
+        gv = int((case.gather_indices >= 0).sum())
+        gb = gv * (4 + case.record + 1024) + (idx.numel() - gv) * (4 + 1024)
+        add(case.name, f"gather {case.record} B", idx.numel(), gv, gb,
+            lambda: B.kvrec_gather(kc, idx, out=o))
+        del backing, kc, kv, o
+        torch.cuda.empty_cache()
+    tk = W.topk_gather()
+    backing, kc = B.alloc_cache(tk.num_blocks, tk.block_size, tk.record, tk.page_stride, device=dev)
+    cs = up(tk.cos_sin())
+    for k in range(tk.num_chunks):
+        kvb, sl, ps = tk.fill_chunk(k)
+        B.kvrec_insert(up(kvb.view(np.int16)).view(torch.bfloat16), kc, up(sl), up(ps), cs,
+                       tk.block_size)
+    idx = up(tk.indices)
+    o = torch.empty(tuple(idx.shape) + (512,), dtype=torch.bfloat16, device=dev)
+    gv = int((tk.indices >= 0).sum())
+    gb = gv * (4 + tk.record + 1024) + (idx.numel() - gv) * (4 + 1024)
+    add(tk.name + " (32768 pages)", "gather 528 B", idx.numel(), gv, gb,
+        lambda: B.kvrec_gather(kc, idx, out=o))
+    del backing, kc, o, flush
+    torch.cuda.empty_cache()
+    print(f"{'workload':28s} {'op':14s} {'rows':>7s} {'cold us':>8s} {'GB/s':>6s} "
+          f"{'%peak':>6s} {'replay us':>9s} {'GB/s':>6s} {'%peak':>6s}", file=out)
+    for r in rows:
+        print(f"{r['workload']:28s} {r['op']:14s} {r['rows']:7d} {r['cold_us']:8.1f} "
+              f"{r['cold_GBps']:6.0f} {100 * r['cold_GBps'] / HBM_PEAK_GBPS:5.1f}% "
+              f"{r['replayed_us']:9.1f} {r['replayed_GBps']:6.0f} "
+              f"{100 * r['replayed_GBps'] / HBM_PEAK_GBPS:5.1f}%", file=out, flush=True)
+    return rows
+
+
 def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -102,6 +206,8 @@ def main() -> int:
     ap.add_argument("--cpu-sample", type=int, default=TOKENS)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also print per-kernel timings of every workload on stderr")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -218,6 +324,10 @@ def main() -> int:
         result["device_copy_GBps"] = copy_gbps
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, backing, out, min(args.cpu_sample, TOKENS))
+    if args.all_configs:
+        del kv, slots, pos, cos_sin, idx, backing, k_cache, out
+        torch.cuda.empty_cache()
+        all_configs_report(dev)
     print(json.dumps(result), flush=True)
     return 0
 
