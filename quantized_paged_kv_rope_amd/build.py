@@ -5,6 +5,8 @@ Flags that matter for bit-exact results:
                                    two rounded products and one rounded add)
   -fno-gpu-flush-denormals-to-zero fp32 denormals kept (inputs and results)
   -target-feature -packed-fp32-ops no v_pk_{add,mul,fma}_f32 generated
+Performance flag:
+  -amdgpu-kernarg-preload-count=16 kernel arguments arrive in SGPRs
 """
 from __future__ import annotations
 
@@ -26,6 +28,8 @@ COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # gfx950 loads the leading kernel arguments into SGPRs at wave launch
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

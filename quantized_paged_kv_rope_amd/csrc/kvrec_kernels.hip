@@ -175,13 +175,13 @@ __device__ __forceinline__ uint32_t lane_read(uint32_t v, int src_lane) {
 // the contiguous range [x * G/8, (x+1) * G/8) keeps the small per-token
 // arrays (slots, positions, indices: 16..32 tokens per 128 B line) and the
 // 16 B scale rows of neighbouring tokens in one L2 instead of eight. The grid
-// is padded to a multiple of 8 blocks; the padding blocks find no work.
+// is padded to a multiple of 8 blocks (per_xcd = grid / 8, passed in); the
+// padding blocks find no work.
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int64_t xcd_block() {
+__device__ __forceinline__ uint32_t xcd_block(uint32_t per_xcd) {
   const uint32_t b = blockIdx.x;
-  const uint32_t per_xcd = gridDim.x / kXcds;
-  return static_cast<int64_t>(b % kXcds) * per_xcd + b / kXcds;
+  return (b % kXcds) * per_xcd + b / kXcds;
 }
 
 // Largest |x| of this lane's 8 values, as fp32 bits (compares as unsigned
@@ -321,11 +321,20 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
 // positions), then the cos/sin rows (which need the positions), and only
 // then encodes and stores. A token whose slot is negative (or out of range)
 // or whose position is out of range is skipped.
+// Kernel arguments are plain scalars, ordered so that the ones every wave
+// needs first (count, block numbering, input pointers) come first: gfx950
+// preloads the leading kernel arguments into SGPRs at wave launch, which
+// saves each wave a dependent kernarg load before its first memory request.
 template <int P, int W, int T, bool kLegacy>
-__global__ __launch_bounds__(W * kWave) void insert_kernel(const InsertArgs a) {
+__global__ __launch_bounds__(W * kWave) void insert_kernel(
+    uint32_t n, uint32_t per_xcd, const u32x4 *kv, const int64_t *slots, const int64_t *positions,
+    const f32x4 *cos_sin, uint32_t max_pos, uint32_t total_slots, uint8_t *base,
+    int64_t page_stride, uint32_t block_size, uint32_t div_magic, uint32_t div_shift) {
+  const InsertArgs a{kv,         slots,       positions, cos_sin,   base,    page_stride, n,
+                     block_size, total_slots, div_magic, div_shift, max_pos};
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const uint32_t t0 = (static_cast<uint32_t>(xcd_block()) * W + wave) * T;
+  const uint32_t t0 = (xcd_block(per_xcd) * W + wave) * T;
   if (t0 >= a.n) return;
 
   u32x4 raw[T];
@@ -380,13 +389,18 @@ __device__ __forceinline__ u32x4 decode_e4m3x8(const u32x2 codes, uint32_t scale
 // handles kRows consecutive output rows: all index loads first, then all
 // record loads, then the decodes and stores.
 template <bool kLegacy, int kRows, int P, int W>
-__global__ __launch_bounds__(W * kWave) void gather_kernel(const GatherArgs a) {
+__global__ __launch_bounds__(W * kWave) void gather_kernel(
+    uint32_t n, uint32_t per_xcd, const int32_t *indices, const uint8_t *base, int64_t page_stride,
+    u32x4 *out, uint32_t total_slots, uint32_t block_size, uint32_t div_magic,
+    uint32_t div_shift) {
+  const GatherArgs a{indices, out, base, page_stride, n, block_size, total_slots, div_magic,
+                     div_shift};
   constexpr bool NT = (P & kNtRecord) != 0;
   constexpr uint32_t kRowBytes = kLegacy ? 576u : 512u;
   constexpr uint32_t kScaleBytes = kLegacy ? 8u : 16u;
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const uint32_t j0 = (static_cast<uint32_t>(xcd_block()) * W + wave) * kRows;
+  const uint32_t j0 = (xcd_block(per_xcd) * W + wave) * kRows;
   if (j0 >= a.n) return;
 
   int32_t idx[kRows];
@@ -446,47 +460,46 @@ constexpr int kGatherPolicy = kNtOut;
 constexpr int kGatherWaves = 2;
 constexpr int kGatherRows = 2;    // rows per wave
 
-// Launches `kernel` with blocks of W waves over `waves` waves; the grid is
-// padded to a whole number of blocks per XCD (see xcd_block).
-template <int W, typename Args>
-hipError_t launch(void (*kernel)(const Args), const Args &a, int64_t waves, hipStream_t stream) {
-  void *params[] = {const_cast<Args *>(&a)};
+// Grid of `waves` waves in blocks of W, padded to a whole number of blocks
+// per XCD (see xcd_block).
+template <int W>
+dim3 xcd_grid(int64_t waves, uint32_t *per_xcd) {
   const int64_t blocks = (waves + W - 1) / W;
-  const dim3 grid(static_cast<unsigned>((blocks + kXcds - 1) / kXcds * kXcds));
-  return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(W * kWave), params, 0,
-                         stream);
+  *per_xcd = static_cast<uint32_t>((blocks + kXcds - 1) / kXcds);
+  return dim3(*per_xcd * kXcds);
 }
 
-InsertArgs make_insert_args(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
-                            const int64_t *positions, const float *cos_sin, int64_t max_pos) {
-  InsertArgs a;
-  a.kv = static_cast<const u32x4 *>(kv);
-  a.slots = slots;
-  a.positions = positions;
-  a.cos_sin = reinterpret_cast<const f32x4 *>(cos_sin);
-  a.base = g.base;
-  a.page_stride = g.page_stride;
-  a.n = static_cast<uint32_t>(n);
-  a.block_size = g.block_size;
-  a.total_slots = g.total_slots;
-  a.div_magic = g.div_magic;
-  a.div_shift = g.div_shift;
-  a.max_pos = static_cast<uint32_t>(max_pos);
-  return a;
+template <int P, int W, int T, bool kLegacy>
+hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
+                         const int64_t *positions, const float *cos_sin, int64_t max_pos,
+                         hipStream_t stream) {
+  uint32_t per_xcd = 0;
+  const dim3 grid = xcd_grid<W>((n + T - 1) / T, &per_xcd);
+  uint32_t n32 = static_cast<uint32_t>(n), mp = static_cast<uint32_t>(max_pos);
+  const u32x4 *kv4 = static_cast<const u32x4 *>(kv);
+  const f32x4 *cs4 = reinterpret_cast<const f32x4 *>(cos_sin);
+  uint8_t *base = g.base;
+  int64_t stride = g.page_stride;
+  uint32_t total = g.total_slots, bs = g.block_size, magic = g.div_magic, shift = g.div_shift;
+  void *params[] = {&n32,  &per_xcd, &kv4,   &slots, &positions, &cs4,  &mp,
+                    &total, &base,    &stride, &bs,    &magic,     &shift};
+  return hipLaunchKernel(reinterpret_cast<const void *>(insert_kernel<P, W, T, kLegacy>), grid,
+                         dim3(W * kWave), params, 0, stream);
 }
 
-GatherArgs make_gather_args(const CacheGeom &g, const int32_t *indices, int64_t n, void *out) {
-  GatherArgs a;
-  a.indices = indices;
-  a.out = static_cast<u32x4 *>(out);
-  a.base = g.base;
-  a.page_stride = g.page_stride;
-  a.n = static_cast<uint32_t>(n);
-  a.block_size = g.block_size;
-  a.total_slots = g.total_slots;
-  a.div_magic = g.div_magic;
-  a.div_shift = g.div_shift;
-  return a;
+template <bool kLegacy, int R, int P, int W>
+hipError_t launch_gather(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
+                         hipStream_t stream) {
+  uint32_t per_xcd = 0;
+  const dim3 grid = xcd_grid<W>((n + R - 1) / R, &per_xcd);
+  uint32_t n32 = static_cast<uint32_t>(n);
+  const uint8_t *base = g.base;
+  int64_t stride = g.page_stride;
+  u32x4 *out4 = static_cast<u32x4 *>(out);
+  uint32_t total = g.total_slots, bs = g.block_size, magic = g.div_magic, shift = g.div_shift;
+  void *params[] = {&n32, &per_xcd, &indices, &base, &stride, &out4, &total, &bs, &magic, &shift};
+  return hipLaunchKernel(reinterpret_cast<const void *>(gather_kernel<kLegacy, R, P, W>), grid,
+                         dim3(W * kWave), params, 0, stream);
 }
 
 }  // namespace
@@ -494,33 +507,25 @@ GatherArgs make_gather_args(const CacheGeom &g, const int32_t *indices, int64_t 
 hipError_t launch_insert_mxfp8(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
                                const int64_t *positions, const float *cos_sin, int64_t max_pos,
                                hipStream_t stream) {
-  return launch<kInsertWaves>(
-      insert_kernel<kInsertPolicy, kInsertWaves, kInsertTokens, false>,
-      make_insert_args(kv, n, g, slots, positions, cos_sin, max_pos),
-      (n + kInsertTokens - 1) / kInsertTokens, stream);
+  return launch_insert<kInsertPolicy, kInsertWaves, kInsertTokens, false>(
+      kv, n, g, slots, positions, cos_sin, max_pos, stream);
 }
 
 hipError_t launch_insert_legacy(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
                                 const int64_t *positions, const float *cos_sin, int64_t max_pos,
                                 hipStream_t stream) {
-  return launch<kInsertWaves>(
-      insert_kernel<kInsertPolicy, kInsertWaves, kInsertTokens, true>,
-      make_insert_args(kv, n, g, slots, positions, cos_sin, max_pos),
-      (n + kInsertTokens - 1) / kInsertTokens, stream);
+  return launch_insert<kInsertPolicy, kInsertWaves, kInsertTokens, true>(
+      kv, n, g, slots, positions, cos_sin, max_pos, stream);
 }
 
 hipError_t launch_gather_mxfp8(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
                                hipStream_t stream) {
-  return launch<kGatherWaves>(gather_kernel<false, kGatherRows, kGatherPolicy, kGatherWaves>,
-                              make_gather_args(g, indices, n, out),
-                              (n + kGatherRows - 1) / kGatherRows, stream);
+  return launch_gather<false, kGatherRows, kGatherPolicy, kGatherWaves>(g, indices, n, out, stream);
 }
 
 hipError_t launch_gather_legacy(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
                                 hipStream_t stream) {
-  return launch<kGatherWaves>(gather_kernel<true, kGatherRows, kGatherPolicy, kGatherWaves>,
-                              make_gather_args(g, indices, n, out),
-                              (n + kGatherRows - 1) / kGatherRows, stream);
+  return launch_gather<true, kGatherRows, kGatherPolicy, kGatherWaves>(g, indices, n, out, stream);
 }
 
 }  // namespace kvrec
