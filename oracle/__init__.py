@@ -25,6 +25,19 @@ RECORD_LEGACY = 584
 
 _lib = None
 
+ROPE = {"neox": 0, "interleaved": 1, "none": 2}
+
+
+class InsertOptions(ctypes.Structure):
+    """orc_insert_options: see kvrec_oracle.h."""
+
+    _fields_ = [("rope", ctypes.c_int32), ("compress_ratio", ctypes.c_int32),
+                ("amax_floor", ctypes.c_float), ("sanitize_nans", ctypes.c_int32)]
+
+
+def options(rope="neox", compress_ratio=1, amax_floor=0.0, sanitize_nans=False) -> InsertOptions:
+    return InsertOptions(ROPE[rope], int(compress_ratio), float(amax_floor), int(bool(sanitize_nans)))
+
 
 def build(verbose: bool = False) -> str:
     """Compile ``liboracle.so`` with strict IEEE float semantics."""
@@ -73,6 +86,11 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_scale_exponent.restype = ctypes.c_int
     L.orc_insert.argtypes = [p, i64, p, i64, i64, i32, i32, p, p, p, i64]
     L.orc_insert.restype = ctypes.c_int
+    L.orc_insert_ex.argtypes = [p, i64, p, i64, i64, i32, i32, p, p, p, i64,
+                                ctypes.POINTER(InsertOptions)]
+    L.orc_insert_ex.restype = ctypes.c_int
+    L.orc_rope_rows_ex.argtypes = [p, i64, p, p, ctypes.POINTER(InsertOptions), p]
+    L.orc_rope_rows_ex.restype = None
     L.orc_gather.argtypes = [p, i64, i64, i32, i32, p, i64, p]
     L.orc_gather.restype = ctypes.c_int
     L.orc_e4m3_encode_f32.argtypes = [p, i64, p]
@@ -162,17 +180,49 @@ def rope_rows(kv_bits: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray) -
     return out
 
 
+def rope_rows_ex(kv_bits: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray,
+                 **opts) -> np.ndarray:
+    """Rotated (and, if asked, NaN-sanitised) fp32 rows under the insert options."""
+    kv_bits = _c(kv_bits, np.uint16)
+    positions = _c(positions, np.int64)
+    cos_sin = _c(cos_sin, np.float32)
+    n = kv_bits.shape[0]
+    o = options(**opts)
+    out = np.empty((n, HEAD_DIM), np.float32)
+    lib().orc_rope_rows_ex(_ptr(kv_bits), n, _ptr(positions), _ptr(cos_sin), ctypes.byref(o),
+                           _ptr(out))
+    return out
+
+
 # ---- the two operations --------------------------------------------------
 
 def insert(kv_bits: np.ndarray, backing: np.ndarray, num_blocks: int, page_stride: int,
-           block_size: int, record: int, slot_mapping: np.ndarray, positions: np.ndarray,
-           cos_sin: np.ndarray) -> None:
+           block_size: int, record: int, slot_mapping: np.ndarray, positions,
+           cos_sin, **opts) -> None:
     """Insert into ``backing`` (uint8, in place; byte 0 = page 0).
 
     Token count = ``slot_mapping.shape[0]``; kv and positions must cover it.
+    Keyword options (rope, compress_ratio, amax_floor, sanitize_nans) select
+    the compressed-KV variant; positions and cos_sin may be None only with
+    rope="none" and compress_ratio 1.
     """
     kv_bits = _c(kv_bits, np.uint16)
     slot_mapping = _c(slot_mapping, np.int64)
+    if positions is None or cos_sin is None:
+        o = options(**opts)
+        if backing.dtype != np.uint8 or not backing.flags.c_contiguous:
+            raise TypeError("backing must be a contiguous uint8 array")
+        n = slot_mapping.shape[0]
+        if kv_bits.ndim != 2 or kv_bits.shape[1] != HEAD_DIM or kv_bits.shape[0] < n:
+            raise ValueError("kv must be [>=n, 512]")
+        pos_p = None if positions is None else _ptr(_c(positions, np.int64))
+        rc = lib().orc_insert_ex(_ptr(kv_bits), n, _ptr(backing), num_blocks, page_stride,
+                                 block_size, record, _ptr(slot_mapping), pos_p, None,
+                                 0 if positions is None else _c(positions, np.int64).shape[0],
+                                 ctypes.byref(o))
+        if rc != 0:
+            raise ValueError("oracle insert rejected the options")
+        return
     positions = _c(positions, np.int64)
     cos_sin = _c(cos_sin, np.float32)
     if backing.dtype != np.uint8 or not backing.flags.c_contiguous:
@@ -186,11 +236,17 @@ def insert(kv_bits: np.ndarray, backing: np.ndarray, num_blocks: int, page_strid
         raise ValueError("cos_sin_cache must be [max_pos, 64]")
     if backing.size < (num_blocks - 1) * page_stride + block_size * record and num_blocks > 0:
         raise ValueError("backing too small for the cache geometry")
-    rc = lib().orc_insert(_ptr(kv_bits), n, _ptr(backing), num_blocks, page_stride, block_size,
-                          record, _ptr(slot_mapping), _ptr(positions), _ptr(cos_sin),
-                          cos_sin.shape[0])
+    if opts:
+        o = options(**opts)
+        rc = lib().orc_insert_ex(_ptr(kv_bits), n, _ptr(backing), num_blocks, page_stride,
+                                 block_size, record, _ptr(slot_mapping), _ptr(positions),
+                                 _ptr(cos_sin), cos_sin.shape[0], ctypes.byref(o))
+    else:
+        rc = lib().orc_insert(_ptr(kv_bits), n, _ptr(backing), num_blocks, page_stride,
+                              block_size, record, _ptr(slot_mapping), _ptr(positions),
+                              _ptr(cos_sin), cos_sin.shape[0])
     if rc != 0:
-        raise ValueError(f"oracle insert rejected record={record}")
+        raise ValueError(f"oracle insert rejected record={record} options={opts}")
 
 
 def gather(backing: np.ndarray, num_blocks: int, page_stride: int, block_size: int,

@@ -161,15 +161,52 @@ static void rope_row(const uint16_t *kv_row, const float *cs_row, float *r) {
   }
 }
 
+/* The compressed-KV insert's rotation ([MXFP8 record] 关键源码片段): the
+ * row is viewed as 256 (even, odd) neighbour pairs; pairs 0..223 are the
+ * NoPE dims and use (cos, sin) = (1, 0), pairs 224..255 use row[p - 224] and
+ * row[32 + p - 224]. Every pair goes through the same two products and one
+ * add/subtract, NoPE pairs included (so, e.g., a -0 whose partner is
+ * negative comes out +0):
+ *   r[2p] = (x[2p] * c) - (x[2p+1] * s),  r[2p+1] = (x[2p+1] * c) + (x[2p] * s). */
+static void rope_row_interleaved(const uint16_t *kv_row, const float *cs_row, float *r) {
+  int p;
+  for (p = 0; p < HEAD_DIM / 2; ++p) {
+    float xe = widen_bf16(kv_row[2 * p]);
+    float xo = widen_bf16(kv_row[2 * p + 1]);
+    int q = p - (NOPE_DIM / 2);
+    float c = q >= 0 ? cs_row[q] : 1.0f;
+    float s = q >= 0 ? cs_row[HALF_ROPE + q] : 0.0f;
+    float xec = xe * c;
+    float xos = xo * s;
+    float xoc = xo * c;
+    float xes = xe * s;
+    r[2 * p] = xec - xos;
+    r[2 * p + 1] = xoc + xes;
+  }
+}
+
+static void rotate_row(const uint16_t *kv_row, const float *cs_row, int32_t rope, float *r) {
+  int d;
+  if (rope == ORC_ROPE_NEOX) {
+    rope_row(kv_row, cs_row, r);
+  } else if (rope == ORC_ROPE_INTERLEAVED) {
+    rope_row_interleaved(kv_row, cs_row, r);
+  } else {
+    for (d = 0; d < HEAD_DIM; ++d) r[d] = widen_bf16(kv_row[d]);
+  }
+}
+
 /* Quantise dims [first, first+width) of r as one group: returns the scale
  * byte and writes width e4m3 codes. The element code is the e4m3fn value
- * nearest to the exact product r * 2^-e. */
-static uint8_t quantise_group(const float *r, int first, int width,
+ * nearest to the exact product r * 2^-e. The group amax is raised to
+ * amax_floor first (the excerpt's floor is 1e-4; 0 leaves it unchanged). */
+static uint8_t quantise_group(const float *r, int first, int width, float amax_floor,
                               uint8_t *codes) {
   float amax = 0.0f;
   int d, e;
   for (d = first; d < first + width; ++d)
     if (fabsf(r[d]) > amax) amax = fabsf(r[d]);
+  if (amax < amax_floor) amax = amax_floor;
   e = orc_scale_exponent(amax);
   for (d = first; d < first + width; ++d)
     codes[d - first] = orc_e4m3_encode(ldexp((double)r[d], -e));
@@ -201,22 +238,55 @@ int orc_insert(const uint16_t *kv, int64_t n, uint8_t *cache,
                int32_t record, const int64_t *slot_mapping,
                const int64_t *positions, const float *cos_sin_cache,
                int64_t max_pos) {
+  orc_insert_options defaults = {ORC_ROPE_NEOX, 1, 0.0f, 0};
+  return orc_insert_ex(kv, n, cache, num_blocks, page_stride, block_size, record,
+                       slot_mapping, positions, cos_sin_cache, max_pos, &defaults);
+}
+
+/* Options beyond the defaults follow the compressed-KV insert of
+ * [MXFP8 record] 关键源码片段: a token is written only when
+ * (position + 1) % R == 0, and it is rotated with table row position / R * R;
+ * the rotated values are NaN-sanitised (NaN -> +0) if asked, before the
+ * group amax (raised to the floor) picks the scale. The scale byte cap (254
+ * when sanitising, 255 otherwise) cannot bind: e <= 127 already. With no
+ * rotation the table is unused and the positions only serve the ratio gate;
+ * with ratio 1 both may be NULL (the no-RoPE K insert of [MXFP8 record]
+ * 实现拆解 4). */
+int orc_insert_ex(const uint16_t *kv, int64_t n, uint8_t *cache, int64_t num_blocks,
+                  int64_t page_stride, int32_t block_size, int32_t record,
+                  const int64_t *slot_mapping, const int64_t *positions,
+                  const float *cos_sin_cache, int64_t max_pos,
+                  const orc_insert_options *opts) {
   int64_t t;
   int64_t total_slots = num_blocks * (int64_t)block_size;
+  int64_t ratio = opts->compress_ratio;
   if (record != V41_RECORD && record != V4_RECORD) return -1;
+  if (ratio < 1 || opts->rope < ORC_ROPE_NEOX || opts->rope > ORC_ROPE_NONE) return -1;
+  /* positions (and the table) may be absent only with no rotation and ratio 1 */
+  if (positions == NULL && (opts->rope != ORC_ROPE_NONE || ratio != 1)) return -1;
 
   for (t = 0; t < n; ++t) {
     float r[HEAD_DIM];
     int64_t slot = slot_mapping[t];
-    int64_t pos = positions[t];
+    int64_t pos = positions != NULL ? positions[t] : 0;
+    int64_t row;
     int64_t page, off;
     uint8_t *pg;
-    int g, i;
+    int g, i, d;
 
     if (slot < 0 || slot >= total_slots) continue;
-    if (pos < 0 || pos >= max_pos) continue;
+    if (positions != NULL) {
+      if (pos < 0 || pos >= max_pos) continue;
+      if ((pos + 1) % ratio != 0) continue;
+    }
+    row = pos / ratio * ratio;
 
-    rope_row(kv + t * HEAD_DIM, cos_sin_cache + pos * ROPE_DIM, r);
+    rotate_row(kv + t * HEAD_DIM,
+               opts->rope == ORC_ROPE_NONE ? NULL : cos_sin_cache + row * ROPE_DIM, opts->rope,
+               r);
+    if (opts->sanitize_nans)
+      for (d = 0; d < HEAD_DIM; ++d)
+        if (r[d] != r[d]) r[d] = 0.0f;
 
     page = slot / block_size;
     off = slot % block_size;
@@ -226,12 +296,12 @@ int orc_insert(const uint16_t *kv, int64_t n, uint8_t *cache,
       uint8_t *data = pg + off * 512;
       uint8_t *scales = pg + (int64_t)block_size * 512 + off * 16;
       for (g = 0; g < 16; ++g)
-        scales[g] = quantise_group(r, g * 32, 32, data + g * 32);
+        scales[g] = quantise_group(r, g * 32, 32, opts->amax_floor, data + g * 32);
     } else {
       uint8_t *data = pg + off * 576;
       uint8_t *scales = pg + (int64_t)block_size * 576 + off * 8;
       for (g = 0; g < 7; ++g)
-        scales[g] = quantise_group(r, g * 64, 64, data + g * 64);
+        scales[g] = quantise_group(r, g * 64, 64, opts->amax_floor, data + g * 64);
       scales[7] = 0;
       for (i = 0; i < ROPE_DIM; ++i) {
         uint16_t h = orc_bf16_round((double)r[NOPE_DIM + i]);
@@ -328,6 +398,19 @@ void orc_bf16_round_f32(const float *x, int64_t n, uint16_t *out) {
 void orc_scale_exponent_f32(const float *amax, int64_t n, int32_t *out) {
   int64_t i;
   for (i = 0; i < n; ++i) out[i] = orc_scale_exponent(amax[i]);
+}
+
+void orc_rope_rows_ex(const uint16_t *kv, int64_t n, const int64_t *positions,
+                      const float *cos_sin_cache, const orc_insert_options *opts, float *out) {
+  int64_t t;
+  int d;
+  for (t = 0; t < n; ++t) {
+    int64_t row = positions[t] / opts->compress_ratio * opts->compress_ratio;
+    rotate_row(kv + t * HEAD_DIM, cos_sin_cache + row * ROPE_DIM, opts->rope, out + t * HEAD_DIM);
+    if (opts->sanitize_nans)
+      for (d = 0; d < HEAD_DIM; ++d)
+        if (out[t * HEAD_DIM + d] != out[t * HEAD_DIM + d]) out[t * HEAD_DIM + d] = 0.0f;
+  }
 }
 
 void orc_rope_rows(const uint16_t *kv, int64_t n, const int64_t *positions,

@@ -57,6 +57,24 @@ int orc_insert(const uint16_t *kv, int64_t n, uint8_t *cache,
                const int64_t *positions, const float *cos_sin_cache,
                int64_t max_pos);
 
+/* Options of the insert. The defaults (NEOX, 1, 0.0f, 0) are orc_insert.
+ * The other settings follow the compressed-KV insert printed in
+ * [MXFP8 record] 关键源码片段 (its "_rope_quant_insert_mxfp8_kernel"). */
+enum { ORC_ROPE_NEOX = 0, ORC_ROPE_INTERLEAVED = 1, ORC_ROPE_NONE = 2 };
+typedef struct orc_insert_options {
+  int32_t rope;           /* pairing of the 64 rotated dims, or no rotation  */
+  int32_t compress_ratio; /* >= 1: write only tokens with (pos+1) % R == 0,
+                             rotating with cos/sin row pos / R * R         */
+  float amax_floor;       /* group amax = max(amax, floor); 0 = no floor     */
+  int32_t sanitize_nans;  /* 1: rotated NaN -> +0, scale byte capped at 254 */
+} orc_insert_options;
+
+int orc_insert_ex(const uint16_t *kv, int64_t n, uint8_t *cache, int64_t num_blocks,
+                  int64_t page_stride, int32_t block_size, int32_t record,
+                  const int64_t *slot_mapping, const int64_t *positions,
+                  const float *cos_sin_cache, int64_t max_pos,
+                  const orc_insert_options *opts);
+
 /* Gather n records back to bf16 rows.
  *   token_indices [n] int32, page * block_size + offset; negative -> zeros
  *   out           bf16 bits [n, 512]
@@ -74,6 +92,8 @@ void orc_bf16_round_f32(const float *x, int64_t n, uint16_t *out);
 void orc_scale_exponent_f32(const float *amax, int64_t n, int32_t *out);
 void orc_rope_rows(const uint16_t *kv, int64_t n, const int64_t *positions,
                    const float *cos_sin_cache, float *out);
+void orc_rope_rows_ex(const uint16_t *kv, int64_t n, const int64_t *positions,
+                      const float *cos_sin_cache, const orc_insert_options *opts, float *out);
 
 #ifdef __cplusplus
 }

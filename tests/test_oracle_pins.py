@@ -453,21 +453,36 @@ def test_independent_vectorised_reference_small_caches():
             assert np.array_equal(got, want), (record, bs)
 
 
-def _vectorised_insert(case):
+def _vectorised_insert(case, kv=None, rope="neox", compress_ratio=1, amax_floor=0.0,
+                       sanitize_nans=False):
+    """Library-primitive restatement (torch casts and elementwise ops, numpy
+    indexing) of the insert and its compressed-KV options."""
+    kv = case.kv_bits if kv is None else kv
     b = case.initial_backing()
-    ok = case.slot_mapping >= 0
+    R = compress_ratio
+    ok = (case.slot_mapping >= 0) & ((case.positions + 1) % R == 0)
     t = np.nonzero(ok)[0]
-    x = torch.from_numpy(case.kv_bits[t].view(np.int16)).view(torch.bfloat16).float()
-    cs = torch.from_numpy(case.cos_sin[case.positions[t]])
+    x = torch.from_numpy(kv[t].view(np.int16)).view(torch.bfloat16).float()
+    rows = case.positions[t] // R * R
+    cs = torch.from_numpy(case.cos_sin[rows])
     c, s = cs[:, :32], cs[:, 32:]
-    x1, x2 = x[:, 448:480].clone(), x[:, 480:].clone()
     r = x.clone()
-    r[:, 448:480] = (x1 * c) - (x2 * s)
-    r[:, 480:] = (x2 * c) + (x1 * s)
+    if rope == "neox":
+        x1, x2 = x[:, 448:480].clone(), x[:, 480:].clone()
+        r[:, 448:480] = (x1 * c) - (x2 * s)
+        r[:, 480:] = (x2 * c) + (x1 * s)
+    elif rope == "interleaved":
+        cc = torch.cat([torch.ones(len(t), 224), c], dim=1)
+        ss = torch.cat([torch.zeros(len(t), 224), s], dim=1)
+        xe, xo = x[:, 0::2].clone(), x[:, 1::2].clone()
+        r[:, 0::2] = (xe * cc) - (xo * ss)
+        r[:, 1::2] = (xo * cc) + (xe * ss)
+    if sanitize_nans:
+        r = torch.where(r == r, r, torch.zeros_like(r))
     fp8 = 512 if case.record == 528 else 448
     gsz = 32 if case.record == 528 else 64
     g = r[:, :fp8].reshape(len(t), -1, gsz).double()
-    amax = g.abs().amax(dim=2)
+    amax = torch.clamp(g.abs().amax(dim=2), min=float(np.float32(amax_floor)))
     e = torch.where(amax == 0, torch.zeros_like(amax),
                     torch.clamp(torch.ceil(torch.log2(amax.clamp_min(1e-300) / 448)), -127, 127))
     y = (g * torch.exp2(-e)[:, :, None]).float().clamp(-448, 448)
@@ -513,3 +528,157 @@ def test_gather_all_code_scale_pairs_vs_library():
     sc = torch.exp2(torch.tensor([float(s) - 127 for s, _ in recs], dtype=torch.float64))
     want = (dec * sc[:, None]).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(out, want)
+
+
+# --------------------------------------------------------------------------
+# The compressed-KV insert variant ([MXFP8 record] 关键源码片段): interleaved
+# pairing, compress-ratio gating, the 1e-4 amax floor, NaN sanitising, and
+# the rotation-free K insert.
+# --------------------------------------------------------------------------
+
+def _compressed_golden_inputs(g):
+    inp = g["compressed_variant"]["inputs"]
+    x = np.zeros((2, 512), np.float32)
+    for d, v in inp["kv_nonzero_token0"]:
+        x[0, d] = float(v)
+    x[1, :] = 1.0
+    kv = _torch_bf16(x)
+    table = np.zeros((inp["max_pos"], 64), np.float32)
+    table[:, :32] = 1.0
+    table[4, 0], table[4, 32], table[4, 1], table[4, 33] = 0.5, 0.75, 0.0, 1.0
+    slots = np.array([t["slot"] for t in inp["tokens"]], np.int64)
+    pos = np.array([t["position"] for t in inp["tokens"]], np.int64)
+    return kv, table, slots, pos
+
+
+@pytest.mark.parametrize("record", [528, 584])
+def test_compressed_variant_worked_token(golden, record):
+    cv = golden["compressed_variant"]
+    kv, table, slots, pos = _compressed_golden_inputs(golden)
+    exp = cv["mxfp8_record" if record == 528 else "legacy_record"]
+    bs, nb = cv["inputs"]["block_size"], cv["inputs"]["num_blocks"]
+    for fill in (0x00, 0x5A):
+        b = np.full(nb * exp["page_stride"], fill, np.uint8)
+        oracle.insert(kv, b, nb, exp["page_stride"], bs, record, slots, pos, table, **cv["options"])
+        d0, s0 = exp["data_offset"], exp["scale_offset"]
+        written = np.zeros(b.size, bool)
+        if record == 528:
+            codes = np.zeros(512, np.uint8)
+            for d, c in exp["codes_nonzero"]:
+                codes[d] = c
+            assert b[d0:d0 + 512].tolist() == codes.tolist()
+            assert b[s0:s0 + 16].tolist() == exp["scales"]
+            written[d0:d0 + 512] = written[s0:s0 + 16] = True
+        else:
+            codes = np.zeros(448, np.uint8)
+            for d, c in exp["codes_nonzero"]:
+                codes[d] = c
+            assert b[d0:d0 + 448].tolist() == codes.tolist()
+            tail = np.zeros(64, np.uint16)
+            for i, h in exp["rope_bf16"]:
+                tail[i] = h
+            assert b[d0 + 448:d0 + 576].view(np.uint16).tolist() == tail.tolist()
+            assert b[s0:s0 + 8].tolist() == exp["scale_row"]
+            written[d0:d0 + 576] = written[s0:s0 + 8] = True
+        # the gated-out token (slot 1) and everything else keep the pre-fill
+        assert (b[~written] == fill).all()
+
+
+def test_interleaved_exact_tables():
+    n, P = 128, 6
+    x = np.clip(RNG.standard_normal((n, 512)), -4, 4).astype(np.float32)
+    kv = _torch_bf16(x)
+    xf = _bf16_to_f32(kv).astype(np.float64)
+    table = np.zeros((P, 64), np.float32)
+    table[:, :32] = RNG.integers(-8, 9, (P, 32)) / 8.0
+    table[:, 32:] = RNG.integers(-8, 9, (P, 32)) / 8.0
+    pos = RNG.integers(0, P, n)
+    r = oracle.rope_rows_ex(kv, pos, table, rope="interleaved").astype(np.float64)
+    c, s = table[pos, :32].astype(np.float64), table[pos, 32:].astype(np.float64)
+    xe, xo = xf[:, 448::2], xf[:, 449::2]
+    assert np.array_equal(r[:, 448::2], xe * c - xo * s)
+    assert np.array_equal(r[:, 449::2], xo * c + xe * s)
+    nz = xf[:, :448] != 0
+    assert np.array_equal(r[:, :448][nz], xf[:, :448][nz])  # NoPE pairs: (1, 0)
+    assert np.array_equal(oracle.rope_rows_ex(kv, pos, table, rope="none"), _bf16_to_f32(kv))
+
+
+def test_compress_ratio_gates_tokens_and_picks_the_row():
+    """Exactly the tokens with (pos + 1) % R == 0 are written, and each is
+    rotated with row pos // R * R: a table whose rows all differ (few-bit
+    values, so products are exact) identifies the row from the result."""
+    R, n, bs, nb = 4, 96, 8, 16
+    case = W.custom_insert(77, n, 528, bs, nb, max_pos=64, drop_frac=0.1)
+    table = np.zeros((64, 64), np.float32)
+    table[:, :32] = RNG.integers(-8, 9, (64, 32)) / 8.0
+    table[:, 32:] = RNG.integers(-8, 9, (64, 32)) / 8.0
+    case.cos_sin = table
+    kv = _torch_bf16(np.clip(_bf16_to_f32(case.kv_bits), -4, 4))
+    b0 = case.initial_backing()
+    b = b0.copy()
+    oracle.insert(kv, b, nb, case.page_stride, bs, 528, case.slot_mapping, case.positions, table,
+                  compress_ratio=R)
+    gate = ((case.positions + 1) % R == 0) & (case.slot_mapping >= 0)
+    written = _record_mask(case, case.slot_mapping[gate])
+    assert (b[~written] == b0[~written]).all()
+    # compare each written record with a ratio-1 insert of the same token at row pos // R * R
+    for t in np.nonzero(gate)[0]:
+        one = b0.copy()
+        oracle.insert(kv[t:t + 1], one, nb, case.page_stride, bs, 528, case.slot_mapping[t:t + 1],
+                      np.array([case.positions[t] // R * R]), table)
+        m = _record_mask(case, case.slot_mapping[t:t + 1])
+        assert np.array_equal(b[m], one[m]), t
+    assert gate.sum() > 10
+
+
+def test_amax_floor_closed_form():
+    assert oracle.scale_exponent(np.float32(1e-4)) == -22  # ceil(log2(1e-4 / 448)) = -22
+    x = np.zeros((1, 512), np.float32)
+    x[0, 0] = 5e-5  # below the floor
+    kv = _torch_bf16(x)
+    v = float(_bf16_to_f32(kv)[0, 0])
+    b = np.zeros(2048, np.uint8)
+    oracle.insert(kv, b, 1, 2048, 2, 528, np.array([0]), np.array([0]), W.rope_table(1),
+                  amax_floor=1e-4)
+    assert b[1024:1040].tolist() == [105] * 16
+    assert b[0] == oracle.e4m3_encode(v * 2.0 ** 22) and (b[1:512] == 0).all()
+    b2 = np.zeros(2048, np.uint8)
+    oracle.insert(kv, b2, 1, 2048, 2, 528, np.array([0]), np.array([0]), W.rope_table(1))
+    assert b2[1024] == oracle.scale_exponent(np.float32(v)) + 127 and b2[1025] == 127
+
+
+VARIANTS = [dict(rope="interleaved", compress_ratio=1, amax_floor=1e-4, sanitize_nans=True),
+            dict(rope="interleaved", compress_ratio=4, amax_floor=1e-4, sanitize_nans=False),
+            dict(rope="neox", compress_ratio=2, amax_floor=0.0, sanitize_nans=True),
+            dict(rope="none", compress_ratio=1, amax_floor=1e-4, sanitize_nans=True),
+            dict(rope="none", compress_ratio=3, amax_floor=0.0, sanitize_nans=False)]
+
+
+@pytest.mark.parametrize("opts", VARIANTS, ids=lambda o: "-".join(str(v) for v in o.values()))
+@pytest.mark.parametrize("record", [528, 584])
+def test_variant_matches_independent_vectorised_reference(opts, record):
+    for bs, nb, n in ((3, 4, 9), (32, 3, 90), (64, 3, 150)):
+        case = W.custom_insert(3000 + bs + n, n, record, bs, nb, max_pos=64, drop_frac=0.2,
+                               scale_rows=True)
+        kv = case.kv_bits.copy()
+        if opts["sanitize_nans"]:
+            kv[RNG.random(kv.shape) < 0.01] = 0x7FC0  # NaN inputs
+        got = case.initial_backing()
+        oracle.insert(kv, got, nb, case.page_stride, bs, record, case.slot_mapping, case.positions,
+                      case.cos_sin, **opts)
+        want = _vectorised_insert(case, kv=kv, **opts)
+        assert np.array_equal(got, want), (record, bs, opts)
+
+
+def test_rotation_free_insert_without_positions():
+    case = W.custom_insert(91, 50, 528, 16, 4)
+    a = case.initial_backing()
+    oracle.insert(case.kv_bits, a, 4, case.page_stride, 16, 528, case.slot_mapping, None, None,
+                  rope="none")
+    b = case.initial_backing()
+    oracle.insert(case.kv_bits, b, 4, case.page_stride, 16, 528, case.slot_mapping,
+                  np.zeros(50, np.int64), W.rope_table(1), rope="none")
+    assert np.array_equal(a, b)
+    with pytest.raises(ValueError):
+        oracle.insert(case.kv_bits, b, 4, case.page_stride, 16, 528, case.slot_mapping, None, None,
+                      rope="interleaved")
