@@ -67,7 +67,8 @@ typedef enum kvrec_status {
   KVREC_ERR_ALIGNMENT = -5,   /* a pointer is not aligned as stated below */
   KVREC_ERR_SIZE = -6,        /* negative count, max_pos < 1, or a size
                                  beyond what the kernels index            */
-  KVREC_ERR_HIP = -7          /* the HIP launch reported an error         */
+  KVREC_ERR_HIP = -7,         /* the HIP launch reported an error         */
+  KVREC_ERR_OPTION = -8       /* an insert option is out of range         */
 } kvrec_status;
 
 /* A paged cache: num_blocks pages, page_stride bytes apart, each holding
@@ -109,7 +110,7 @@ int kvrec_page_stride(int32_t record, int32_t block_size, int64_t *page_stride_o
  *                 cos_sin_cache for each token.
  *   cos_sin_cache (device) fp32 [max_pos, 64]: 32 cos values then 32 sin
  *                 values per row; 16-B aligned.
- *   max_pos       rows of cos_sin_cache, >= 1.
+ *   max_pos       rows of cos_sin_cache, 1 .. 2^30.
  *   block_size    must equal k_cache->block_size (cross-check, as the page's
  *                 op keeps k_cache.size(1) == cache_block_size).
  *   record        must equal k_cache->record.
@@ -128,6 +129,47 @@ int kvrec_insert(const void *kv, int64_t num_tokens, const kvrec_cache *k_cache,
                  const int64_t *slot_mapping, const int64_t *positions,
                  const float *cos_sin_cache, int64_t max_pos, int32_t block_size,
                  int32_t record, kvrec_stream stream);
+
+/* Options of kvrec_insert_ex. kvrec_insert is kvrec_insert_ex with
+ * {KVREC_ROPE_NEOX, 1, 0.0f, 0}. The other settings follow the compressed-KV
+ * insert printed in [MXFP8 record] 关键源码片段 (its
+ * "_rope_quant_insert_mxfp8_kernel") and the K insert without RoPE of
+ * [MXFP8 record] 实现拆解 4.
+ *   rope            KVREC_ROPE_NEOX: pairs (448+i, 480+i), dims 0..447 untouched.
+ *                   KVREC_ROPE_INTERLEAVED: neighbour pairs (2p, 2p+1); pairs
+ *                   224..255 rotate with cos row[p-224], sin row[32+p-224];
+ *                   the NoPE pairs go through the same products with
+ *                   (cos, sin) = (1, 0) (a -0 whose partner is negative turns
+ *                   +0; a NaN spreads to its partner).
+ *                   KVREC_ROPE_NONE: no rotation; the table is not read.
+ *   compress_ratio  R in [1, 2^30]: only tokens with (position + 1) % R == 0
+ *                   are written, rotated with table row position / R * R.
+ *   amax_floor      finite, >= 0: each group's amax is raised to it before
+ *                   the exponent is chosen (the excerpt uses 1e-4; 0 = none).
+ *   sanitize_nans   0 or 1: rotated NaNs become +0 before quantisation. */
+typedef enum kvrec_rope {
+  KVREC_ROPE_NEOX = 0,
+  KVREC_ROPE_INTERLEAVED = 1,
+  KVREC_ROPE_NONE = 2
+} kvrec_rope;
+
+typedef struct kvrec_insert_options {
+  int32_t rope;
+  int32_t compress_ratio;
+  float amax_floor;
+  int32_t sanitize_nans;
+} kvrec_insert_options;
+
+/* kvrec_insert with options (NULL = the defaults). Same arguments, layout
+ * and errors as kvrec_insert, plus KVREC_ERR_OPTION for an option out of
+ * range. With rope == KVREC_ROPE_NONE the table is not read and
+ * cos_sin_cache may be NULL; with compress_ratio == 1 as well, positions are
+ * not read either and may be NULL (max_pos is then ignored). */
+int kvrec_insert_ex(const void *kv, int64_t num_tokens, const kvrec_cache *k_cache,
+                    const int64_t *slot_mapping, const int64_t *positions,
+                    const float *cos_sin_cache, int64_t max_pos, int32_t block_size,
+                    int32_t record, const kvrec_insert_options *options,
+                    kvrec_stream stream);
 
 /* Gather num_indices records back to bf16 rows ([MXFP8 record] 实现拆解 4:
  * one gather parameterised by the record; [FlashMLA]: index =

@@ -16,7 +16,10 @@ from .binding import (  # noqa: F401
     alloc_cache,
     cache_descriptor,
     kvrec_gather,
+    insert_options,
     kvrec_insert,
+    kvrec_insert_ex,
+    kvrec_insert_options,
     kvrec_page_stride,
     kvrec_status_str,
     load_library,

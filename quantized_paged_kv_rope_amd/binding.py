@@ -33,14 +33,17 @@ HEAD_DIM = 512
 ROPE_DIM = 64
 RECORD_MXFP8 = 528
 RECORD_LEGACY = 584
+MAX_POS = 1 << 30  # the C ABI's limit on table rows
 
 KVREC_OK = 0
 STATUS_NAMES = {
     0: "KVREC_OK", -1: "KVREC_ERR_NULL", -2: "KVREC_ERR_RECORD", -3: "KVREC_ERR_BLOCK_SIZE",
     -4: "KVREC_ERR_PAGE_STRIDE", -5: "KVREC_ERR_ALIGNMENT", -6: "KVREC_ERR_SIZE",
-    -7: "KVREC_ERR_HIP",
+    -7: "KVREC_ERR_HIP", -8: "KVREC_ERR_OPTION",
 }
-EXPORTED_SYMBOLS = ("kvrec_page_stride", "kvrec_insert", "kvrec_gather", "kvrec_status_str")
+EXPORTED_SYMBOLS = ("kvrec_page_stride", "kvrec_insert", "kvrec_insert_ex", "kvrec_gather",
+                    "kvrec_status_str")
+ROPE = {"neox": 0, "interleaved": 1, "none": 2}
 
 
 class KvrecError(RuntimeError):
@@ -61,6 +64,27 @@ class kvrec_cache(ctypes.Structure):
     ]
 
 
+class kvrec_insert_options(ctypes.Structure):
+    _fields_ = [
+        ("rope", ctypes.c_int32),
+        ("compress_ratio", ctypes.c_int32),
+        ("amax_floor", ctypes.c_float),
+        ("sanitize_nans", ctypes.c_int32),
+    ]
+
+
+def insert_options(rope: str = "neox", compress_ratio: int = 1, amax_floor: float = 0.0,
+                   sanitize_nans: bool = False) -> kvrec_insert_options:
+    """Options of kvrec_insert_ex. The non-default settings follow the
+    compressed-KV insert of [MXFP8 record] 关键源码片段: rope="interleaved",
+    compress_ratio=R, amax_floor=1e-4, sanitize_nans=True; rope="none" is the
+    K insert without RoPE."""
+    if rope not in ROPE:
+        raise ValueError(f"rope must be one of {sorted(ROPE)}")
+    return kvrec_insert_options(ROPE[rope], int(compress_ratio), float(amax_floor),
+                                int(bool(sanitize_nans)))
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -79,6 +103,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvrec_page_stride.restype = ctypes.c_int
     L.kvrec_insert.argtypes = [p, i64, ctypes.POINTER(kvrec_cache), p, p, p, i64, i32, i32, p]
     L.kvrec_insert.restype = ctypes.c_int
+    L.kvrec_insert_ex.argtypes = [p, i64, ctypes.POINTER(kvrec_cache), p, p, p, i64, i32, i32,
+                                  ctypes.POINTER(kvrec_insert_options), p]
+    L.kvrec_insert_ex.restype = ctypes.c_int
     L.kvrec_gather.argtypes = [ctypes.POINTER(kvrec_cache), p, i64, p, p]
     L.kvrec_gather.restype = ctypes.c_int
     L.kvrec_status_str.argtypes = [ctypes.c_int]
@@ -127,13 +154,34 @@ def _stream_handle(device: torch.device) -> int:
 
 
 def kvrec_insert(kv: torch.Tensor, k_cache: torch.Tensor, slot_mapping: torch.Tensor,
-                 positions: torch.Tensor, cos_sin_cache: torch.Tensor, block_size: int,
-                 record: Optional[int] = None) -> None:
+                 positions: Optional[torch.Tensor], cos_sin_cache: Optional[torch.Tensor],
+                 block_size: int, record: Optional[int] = None, *, rope: str = "neox",
+                 compress_ratio: int = 1, amax_floor: float = 0.0,
+                 sanitize_nans: bool = False) -> None:
     """Fused RoPE + quantise + paged insert, in place on ``k_cache``.
 
-    Runs asynchronously on the current stream of ``kv``'s device."""
-    for name, t in (("kv", kv), ("slot_mapping", slot_mapping), ("positions", positions),
-                    ("cos_sin_cache", cos_sin_cache)):
+    Runs asynchronously on the current stream of ``kv``'s device. The keyword
+    options select the compressed-KV variant (see :func:`insert_options`);
+    with the defaults this is the C ``kvrec_insert``."""
+    opts = insert_options(rope, compress_ratio, amax_floor, sanitize_nans)
+    default = (rope == "neox" and compress_ratio == 1 and amax_floor == 0.0
+               and not sanitize_nans)
+    kvrec_insert_ex(kv, k_cache, slot_mapping, positions, cos_sin_cache, block_size, record,
+                    None if default else opts)
+
+
+def kvrec_insert_ex(kv: torch.Tensor, k_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                    positions: Optional[torch.Tensor], cos_sin_cache: Optional[torch.Tensor],
+                    block_size: int, record: Optional[int] = None,
+                    options: Optional[kvrec_insert_options] = None) -> None:
+    """The C ``kvrec_insert_ex``: :func:`kvrec_insert` with an options struct
+    (``None`` = the defaults, which calls the C ``kvrec_insert``)."""
+    tensors = [("kv", kv), ("slot_mapping", slot_mapping)]
+    if positions is not None:
+        tensors.append(("positions", positions))
+    if cos_sin_cache is not None:
+        tensors.append(("cos_sin_cache", cos_sin_cache))
+    for name, t in tensors:
         _require_gpu(t, name)
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
@@ -141,24 +189,34 @@ def kvrec_insert(kv: torch.Tensor, k_cache: torch.Tensor, slot_mapping: torch.Te
         raise TypeError("kv must be bf16 [tokens, 512]")
     if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1:
         raise TypeError("slot_mapping must be a 1-D int64 tensor")
-    if positions.dtype != torch.int64 or positions.dim() != 1:
+    if positions is not None and (positions.dtype != torch.int64 or positions.dim() != 1):
         raise TypeError("positions must be a 1-D int64 tensor")
-    if cos_sin_cache.dtype != torch.float32 or cos_sin_cache.dim() != 2 or \
-            cos_sin_cache.shape[1] != ROPE_DIM:
+    if cos_sin_cache is not None and (cos_sin_cache.dtype != torch.float32 or
+                                      cos_sin_cache.dim() != 2 or
+                                      cos_sin_cache.shape[1] != ROPE_DIM):
         raise TypeError("cos_sin_cache must be fp32 [max_pos, 64]")
     n = slot_mapping.shape[0]
-    if kv.shape[0] < n or positions.shape[0] < n:
+    if kv.shape[0] < n or (positions is not None and positions.shape[0] < n):
         raise ValueError("kv and positions must cover every token of slot_mapping")
-    devs = {t.device for t in (kv, k_cache, slot_mapping, positions, cos_sin_cache)}
+    devs = {t.device for _, t in tensors} | {k_cache.device}
     if len(devs) != 1:
         raise ValueError(f"all tensors must be on one device, got {devs}")
     desc = cache_descriptor(k_cache)
     rec = int(k_cache.shape[2]) if record is None else int(record)
+    pos_p = positions.data_ptr() if positions is not None else None
+    cs_p = cos_sin_cache.data_ptr() if cos_sin_cache is not None else None
+    # Without a table (rotation-free insert) positions only feed the ratio
+    # gate, so they are bounded by the ABI's limit alone.
+    max_pos = cos_sin_cache.shape[0] if cos_sin_cache is not None else MAX_POS
     with torch.cuda.device(kv.device):
-        _check(load_library().kvrec_insert(
-            kv.data_ptr(), n, ctypes.byref(desc), slot_mapping.data_ptr(), positions.data_ptr(),
-            cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], int(block_size), rec,
-            _stream_handle(kv.device)))
+        if options is None:
+            _check(load_library().kvrec_insert(
+                kv.data_ptr(), n, ctypes.byref(desc), slot_mapping.data_ptr(), pos_p, cs_p,
+                max_pos, int(block_size), rec, _stream_handle(kv.device)))
+        else:
+            _check(load_library().kvrec_insert_ex(
+                kv.data_ptr(), n, ctypes.byref(desc), slot_mapping.data_ptr(), pos_p, cs_p,
+                max_pos, int(block_size), rec, ctypes.byref(options), _stream_handle(kv.device)))
 
 
 def kvrec_gather(k_cache: torch.Tensor, token_indices: torch.Tensor,

@@ -7,7 +7,9 @@
 // selects the kernel, the block size is cross-checked against the cache, the
 // page stride must be a multiple of the record's page alignment (512 B for
 // the 528 B record, 576 B for the 584 B record: [MXFP8 record] 功能与动机).
+#include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <hip/hip_runtime.h>
 
@@ -17,7 +19,7 @@
 namespace {
 
 constexpr int64_t kMaxCount = int64_t{1} << 30;  // rows and slots; keeps grids < 2^31 blocks
-constexpr int64_t kMaxPos = int64_t{1} << 31;    // cos/sin rows (a 512 GB table)
+constexpr int64_t kMaxPos = int64_t{1} << 30;    // cos/sin rows (a 256 GB table); pos + 1 < 2^31
 
 bool misaligned(const void *p, uintptr_t align) {
   return (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0;
@@ -79,27 +81,53 @@ int kvrec_insert(const void *kv, int64_t num_tokens, const kvrec_cache *k_cache,
                  const int64_t *slot_mapping, const int64_t *positions,
                  const float *cos_sin_cache, int64_t max_pos, int32_t block_size,
                  int32_t record, kvrec_stream stream) {
+  return kvrec_insert_ex(kv, num_tokens, k_cache, slot_mapping, positions, cos_sin_cache, max_pos,
+                         block_size, record, nullptr, stream);
+}
+
+int kvrec_insert_ex(const void *kv, int64_t num_tokens, const kvrec_cache *k_cache,
+                    const int64_t *slot_mapping, const int64_t *positions,
+                    const float *cos_sin_cache, int64_t max_pos, int32_t block_size,
+                    int32_t record, const kvrec_insert_options *options, kvrec_stream stream) {
   if (k_cache == nullptr) return KVREC_ERR_NULL;
   if (!known_record(record) || record != k_cache->record) return KVREC_ERR_RECORD;
   if (block_size < 1 || block_size != k_cache->block_size) return KVREC_ERR_BLOCK_SIZE;
   kvrec::CacheGeom g;
   const int rc = check_cache(k_cache, &g);
   if (rc != KVREC_OK) return rc;
+  const kvrec_insert_options defaults = {KVREC_ROPE_NEOX, 1, 0.0f, 0};
+  const kvrec_insert_options &opt = options != nullptr ? *options : defaults;
+  if (opt.rope < KVREC_ROPE_NEOX || opt.rope > KVREC_ROPE_NONE) return KVREC_ERR_OPTION;
+  if (opt.compress_ratio < 1 || opt.compress_ratio > kMaxCount) return KVREC_ERR_OPTION;
+  if (!(opt.amax_floor >= 0.0f) || !isfinite(opt.amax_floor)) return KVREC_ERR_OPTION;
+  if (opt.sanitize_nans != 0 && opt.sanitize_nans != 1) return KVREC_ERR_OPTION;
   if (num_tokens < 0 || num_tokens > kMaxCount) return KVREC_ERR_SIZE;
   if (num_tokens == 0) return KVREC_OK;
-  if (kv == nullptr || slot_mapping == nullptr || positions == nullptr || cos_sin_cache == nullptr)
+  // Positions are read for the rotation and the ratio gate; the table only
+  // for the rotation.
+  const bool needs_positions = opt.rope != KVREC_ROPE_NONE || opt.compress_ratio != 1;
+  const bool needs_table = opt.rope != KVREC_ROPE_NONE;
+  if (kv == nullptr || slot_mapping == nullptr) return KVREC_ERR_NULL;
+  if ((needs_positions && positions == nullptr) || (needs_table && cos_sin_cache == nullptr))
     return KVREC_ERR_NULL;
-  if (max_pos < 1 || max_pos > kMaxPos) return KVREC_ERR_SIZE;
+  if (positions != nullptr && (max_pos < 1 || max_pos > kMaxPos)) return KVREC_ERR_SIZE;
   if (misaligned(kv, 16) || misaligned(cos_sin_cache, 16) || misaligned(slot_mapping, 8) ||
       misaligned(positions, 8))
     return KVREC_ERR_ALIGNMENT;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  kvrec::InsertOptions o;
+  o.rope = opt.rope;
+  o.sanitize = opt.sanitize_nans != 0;
+  o.ratio = static_cast<uint32_t>(opt.compress_ratio);
+  division_magic(o.ratio, &o.ratio_magic, &o.ratio_shift);
+  memcpy(&o.amax_floor_bits, &opt.amax_floor, sizeof o.amax_floor_bits);
+  // Without positions (the rotation-free insert with ratio 1) the kernels
+  // skip the position checks; the table is never read without a rotation.
+  const int64_t *pos = needs_positions ? positions : nullptr;
+  if (pos == nullptr) max_pos = 1;
+  if (!needs_table) cos_sin_cache = nullptr;
   const hipError_t err =
-      record == KVREC_RECORD_MXFP8
-          ? kvrec::launch_insert_mxfp8(kv, num_tokens, g, slot_mapping, positions, cos_sin_cache,
-                                       max_pos, s)
-          : kvrec::launch_insert_legacy(kv, num_tokens, g, slot_mapping, positions,
-                                        cos_sin_cache, max_pos, s);
+      kvrec::launch_insert(kv, num_tokens, g, slot_mapping, pos, cos_sin_cache, max_pos,
+                           record == KVREC_RECORD_LEGACY, o, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? KVREC_OK : KVREC_ERR_HIP;
 }
 
@@ -130,6 +158,7 @@ const char *kvrec_status_str(int status) {
     case KVREC_ERR_ALIGNMENT: return "pointer not aligned as the ABI requires";
     case KVREC_ERR_SIZE: return "size out of range";
     case KVREC_ERR_HIP: return "HIP launch error";
+    case KVREC_ERR_OPTION: return "insert option out of range";
     default: return "unknown kvrec status";
   }
 }

@@ -252,15 +252,46 @@ __device__ __forceinline__ void rope_tail(float f[8], const u32x4 raw, int lane,
   }
 }
 
+// Rotation modes: the NeoX half-split pairs (448+i, 480+i) of the insert,
+// the neighbour pairs (2p, 2p+1) of the compressed-KV insert ([MXFP8 record]
+// 关键源码片段), or none (the K insert without RoPE).
+enum : int { kRopeNeox = 0, kRopeInterleaved = 1, kRopeNone = 2 };
+
+// Neighbour-pair rotation. Lane l holds pairs 4l..4l+3 (dims 8l..8l+7), so
+// no lane exchange is needed. As in the excerpt, the NoPE pairs (lanes < 56)
+// go through the same products with (cos, sin) = (1, 0); lane 56+j uses cos
+// row[4j..4j+3] (c0) and sin row[32+4j..32+4j+3] (s0).
+__device__ __forceinline__ void rope_interleaved(float f[8], int lane, const f32x4 c0,
+                                                 const f32x4 s0) {
+  const bool tail = lane >= 56;
+  const float c[4] = {tail ? c0.x : 1.0f, tail ? c0.y : 1.0f, tail ? c0.z : 1.0f,
+                      tail ? c0.w : 1.0f};
+  const float s[4] = {tail ? s0.x : 0.0f, tail ? s0.y : 0.0f, tail ? s0.z : 0.0f,
+                      tail ? s0.w : 0.0f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float xe = f[2 * k], xo = f[2 * k + 1];
+    const float xec = xe * c[k], xos = xo * s[k], xoc = xo * c[k], xes = xe * s[k];
+    f[2 * k] = xec - xos;
+    f[2 * k + 1] = xoc + xes;
+  }
+}
+
 // Encode one loaded token and store its record. `raw` is the lane's 16 B of
 // the bf16 row, c0..s1 the lane's cos/sin values (lanes 56..63 only).
-template <int P, bool kLegacy>
+template <int P, bool kLegacy, int kRope, bool kSanitize, bool kOptions>
 __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, const u32x4 raw,
                                              const f32x4 c0, const f32x4 c1, const f32x4 s0,
-                                             const f32x4 s1, uint32_t slot) {
+                                             const f32x4 s1, uint32_t slot,
+                                             uint32_t amax_floor_bits) {
   float f[8];
   unpack_bf16x8(raw, f);
-  rope_tail(f, raw, lane, c0, c1, s0, s1);
+  if constexpr (kRope == kRopeNeox) rope_tail(f, raw, lane, c0, c1, s0, s1);
+  if constexpr (kRope == kRopeInterleaved) rope_interleaved(f, lane, c0, s0);
+  if constexpr (kSanitize) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) f[k] = f[k] == f[k] ? f[k] : 0.0f;  // NaN -> +0
+  }
   const PageOff po = page_of(slot, a.block_size, a.div_magic, a.div_shift);
   const uint32_t off = po.off;
   uint8_t *page = a.base + static_cast<int64_t>(po.page) * a.page_stride;
@@ -271,6 +302,7 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
   amax = dpp_umax<kQuadXor1>(amax);
   amax = dpp_umax<kQuadXor2>(amax);
   if constexpr (kLegacy) amax = dpp_umax<kHalfRowMirror>(amax);  // 8 lanes = 64 dims
+  if constexpr (kOptions) amax = max(amax, amax_floor_bits);  // the compressed-KV floor
   const int e = scale_exponent(amax);
   const uint32_t b = static_cast<uint32_t>(e + 127);
 
@@ -325,11 +357,14 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
 // needs first (count, block numbering, input pointers) come first: gfx950
 // preloads the leading kernel arguments into SGPRs at wave launch, which
 // saves each wave a dependent kernarg load before its first memory request.
-template <int P, int W, int T, bool kLegacy>
+// kOptions = false is the plain insert (NeoX, ratio 1, no floor, positions
+// present); its code carries none of the option checks below.
+template <int P, int W, int T, bool kLegacy, int kRope, bool kSanitize, bool kOptions>
 __global__ __launch_bounds__(W * kWave) void insert_kernel(
     uint32_t n, uint32_t per_xcd, const u32x4 *kv, const int64_t *slots, const int64_t *positions,
     const f32x4 *cos_sin, uint32_t max_pos, uint32_t total_slots, uint8_t *base,
-    int64_t page_stride, uint32_t block_size, uint32_t div_magic, uint32_t div_shift) {
+    int64_t page_stride, uint32_t block_size, uint32_t div_magic, uint32_t div_shift,
+    uint32_t ratio, uint32_t ratio_magic, uint32_t ratio_shift, uint32_t amax_floor_bits) {
   const InsertArgs a{kv,         slots,       positions, cos_sin,   base,    page_stride, n,
                      block_size, total_slots, div_magic, div_shift, max_pos};
   const int lane = threadIdx.x & (kWave - 1);
@@ -338,7 +373,7 @@ __global__ __launch_bounds__(W * kWave) void insert_kernel(
   if (t0 >= a.n) return;
 
   u32x4 raw[T];
-  uint32_t slot[T], pos[T];
+  uint32_t slot[T], row[T];
   bool ok[T];
 #pragma unroll
   for (int k = 0; k < T; ++k) {
@@ -347,31 +382,49 @@ __global__ __launch_bounds__(W * kWave) void insert_kernel(
     raw[k] = in ? ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t) * kWave + lane)
                 : u32x4{0, 0, 0, 0};
     const int64_t sl = in ? a.slots[t] : -1;
-    const int64_t ps = in ? a.positions[t] : -1;
-    ok[k] = below(sl, a.total_slots) && below(ps, a.max_pos);
+    // No positions: only the rotation-free insert with ratio 1 (host-checked).
+    const bool has_pos = !kOptions || positions != nullptr;
+    const int64_t ps = !has_pos ? 0 : in ? a.positions[t] : -1;
+    ok[k] = below(sl, a.total_slots) && (!has_pos || below(ps, a.max_pos));
     slot[k] = static_cast<uint32_t>(sl);
-    pos[k] = static_cast<uint32_t>(ps);
+    row[k] = static_cast<uint32_t>(ps);
+    if (kOptions && ratio > 1) {
+      // Compressed-KV gate ([MXFP8 record] 关键源码片段): write only when
+      // (pos + 1) % ratio == 0, rotating with row pos / ratio * ratio, which
+      // is then pos + 1 - ratio. pos + 1 <= 2^30, so the division is exact.
+      const uint32_t p1 = row[k] + 1;
+      const uint32_t q = (__umulhi(p1, ratio_magic) + p1) >> ratio_shift;
+      ok[k] = ok[k] && p1 == q * ratio;
+      row[k] = p1 - ratio;
+    }
   }
   // Only lanes 56..63 read (and later use) the cos/sin values. The empty asm
   // statements give the registers an unset value in the other lanes, so the
-  // compiler does not spend 16 moves per token zero-filling them.
+  // compiler does not spend moves per token zero-filling them.
   f32x4 c0[T], c1[T], s0[T], s1[T];
 #pragma unroll
   for (int k = 0; k < T; ++k) {
     asm("" : "=v"(c0[k]), "=v"(c1[k]), "=v"(s0[k]), "=v"(s1[k]));
-    if (ok[k] && lane >= 56) {
-      const f32x4 *row = a.cos_sin + static_cast<uint64_t>(pos[k]) * 16;
-      const int q = 2 * (lane & 3);  // float4 index of cos[8*(lane&3)]
+    if (kRope != kRopeNone && ok[k] && lane >= 56) {
+      const f32x4 *tab = a.cos_sin + static_cast<uint64_t>(row[k]) * 16;
       constexpr bool nt = (P & kNtTable) != 0;
-      c0[k] = ld<nt>(row + q);
-      c1[k] = ld<nt>(row + q + 1);
-      s0[k] = ld<nt>(row + 8 + q);
-      s1[k] = ld<nt>(row + 9 + q);
+      if constexpr (kRope == kRopeNeox) {
+        const int q = 2 * (lane & 3);  // float4 index of cos[8*(lane&3)]
+        c0[k] = ld<nt>(tab + q);
+        c1[k] = ld<nt>(tab + q + 1);
+        s0[k] = ld<nt>(tab + 8 + q);
+        s1[k] = ld<nt>(tab + 9 + q);
+      } else {
+        c0[k] = ld<nt>(tab + (lane - 56));      // cos of pairs 4j..4j+3
+        s0[k] = ld<nt>(tab + 8 + (lane - 56));  // sin of the same pairs
+      }
     }
   }
 #pragma unroll
   for (int k = 0; k < T; ++k)
-    if (ok[k]) encode_store<P, kLegacy>(a, lane, raw[k], c0[k], c1[k], s0[k], s1[k], slot[k]);
+    if (ok[k])
+      encode_store<P, kLegacy, kRope, kSanitize, kOptions>(a, lane, raw[k], c0[k], c1[k], s0[k],
+                                                           s1[k], slot[k], amax_floor_bits);
 }
 
 // bf16 of e4m3fn(code) * 2^(scale_byte - 127) for 8 codes, value k = byte k.
@@ -469,10 +522,10 @@ dim3 xcd_grid(int64_t waves, uint32_t *per_xcd) {
   return dim3(*per_xcd * kXcds);
 }
 
-template <int P, int W, int T, bool kLegacy>
+template <int P, int W, int T, bool kLegacy, int kRope, bool kSanitize, bool kOptions>
 hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
                          const int64_t *positions, const float *cos_sin, int64_t max_pos,
-                         hipStream_t stream) {
+                         const InsertOptions &o, hipStream_t stream) {
   uint32_t per_xcd = 0;
   const dim3 grid = xcd_grid<W>((n + T - 1) / T, &per_xcd);
   uint32_t n32 = static_cast<uint32_t>(n), mp = static_cast<uint32_t>(max_pos);
@@ -481,10 +534,23 @@ hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const in
   uint8_t *base = g.base;
   int64_t stride = g.page_stride;
   uint32_t total = g.total_slots, bs = g.block_size, magic = g.div_magic, shift = g.div_shift;
-  void *params[] = {&n32,  &per_xcd, &kv4,   &slots, &positions, &cs4,  &mp,
-                    &total, &base,    &stride, &bs,    &magic,     &shift};
-  return hipLaunchKernel(reinterpret_cast<const void *>(insert_kernel<P, W, T, kLegacy>), grid,
-                         dim3(W * kWave), params, 0, stream);
+  uint32_t ratio = o.ratio, rmagic = o.ratio_magic, rshift = o.ratio_shift;
+  uint32_t floor_bits = o.amax_floor_bits;
+  void *params[] = {&n32,  &per_xcd, &kv4,  &slots,  &positions, &cs4,   &mp,   &total,     &base,
+                    &stride, &bs,     &magic, &shift, &ratio,     &rmagic, &rshift, &floor_bits};
+  return hipLaunchKernel(
+      reinterpret_cast<const void *>(insert_kernel<P, W, T, kLegacy, kRope, kSanitize, kOptions>),
+      grid,
+      dim3(W * kWave), params, 0, stream);
+}
+
+template <bool kLegacy, int kRope, bool kSanitize, bool kOptions = true>
+hipError_t launch_insert_tuned(const void *kv, int64_t n, const CacheGeom &g,
+                               const int64_t *slots, const int64_t *positions,
+                               const float *cos_sin, int64_t max_pos, const InsertOptions &o,
+                               hipStream_t stream) {
+  return launch_insert<kInsertPolicy, kInsertWaves, kInsertTokens, kLegacy, kRope, kSanitize,
+                       kOptions>(kv, n, g, slots, positions, cos_sin, max_pos, o, stream);
 }
 
 template <bool kLegacy, int R, int P, int W>
@@ -504,18 +570,32 @@ hipError_t launch_gather(const CacheGeom &g, const int32_t *indices, int64_t n, 
 
 }  // namespace
 
-hipError_t launch_insert_mxfp8(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
-                               const int64_t *positions, const float *cos_sin, int64_t max_pos,
-                               hipStream_t stream) {
-  return launch_insert<kInsertPolicy, kInsertWaves, kInsertTokens, false>(
-      kv, n, g, slots, positions, cos_sin, max_pos, stream);
-}
-
-hipError_t launch_insert_legacy(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
-                                const int64_t *positions, const float *cos_sin, int64_t max_pos,
-                                hipStream_t stream) {
-  return launch_insert<kInsertPolicy, kInsertWaves, kInsertTokens, true>(
-      kv, n, g, slots, positions, cos_sin, max_pos, stream);
+hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
+                         const int64_t *positions, const float *cos_sin, int64_t max_pos,
+                         bool legacy, const InsertOptions &o, hipStream_t stream) {
+  // The plain insert has its own instantiation; the options get one per
+  // (record, rotation, sanitise), with ratio and floor as uniform runtime
+  // values.
+  const bool plain = o.rope == kRopeNeox && !o.sanitize && o.ratio == 1 &&
+                     o.amax_floor_bits == 0 && positions != nullptr;
+  if (plain)
+    return legacy ? launch_insert_tuned<true, kRopeNeox, false, false>(
+                        kv, n, g, slots, positions, cos_sin, max_pos, o, stream)
+                  : launch_insert_tuned<false, kRopeNeox, false, false>(
+                        kv, n, g, slots, positions, cos_sin, max_pos, o, stream);
+#define KVREC_INSERT(L, R, S)                                                               \
+  if (legacy == L && o.rope == R && o.sanitize == S)                                        \
+    return launch_insert_tuned<L, R, S>(kv, n, g, slots, positions, cos_sin, max_pos, o, \
+                                        stream);
+#define KVREC_INSERT_R(L, R) KVREC_INSERT(L, R, false) KVREC_INSERT(L, R, true)
+#define KVREC_INSERT_L(L) \
+  KVREC_INSERT_R(L, kRopeNeox) KVREC_INSERT_R(L, kRopeInterleaved) KVREC_INSERT_R(L, kRopeNone)
+  KVREC_INSERT_L(false)
+  KVREC_INSERT_L(true)
+#undef KVREC_INSERT_L
+#undef KVREC_INSERT_R
+#undef KVREC_INSERT
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gather_mxfp8(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,

@@ -17,12 +17,19 @@ struct CacheGeom {
   uint32_t div_shift;    //   for every slot < 2^31
 };
 
-hipError_t launch_insert_mxfp8(const void *kv, int64_t n, const CacheGeom &g,
-                               const int64_t *slots, const int64_t *positions,
-                               const float *cos_sin, int64_t max_pos, hipStream_t stream);
-hipError_t launch_insert_legacy(const void *kv, int64_t n, const CacheGeom &g,
-                                const int64_t *slots, const int64_t *positions,
-                                const float *cos_sin, int64_t max_pos, hipStream_t stream);
+// Validated insert options (see kvrec_insert_options in kvrec.h).
+struct InsertOptions {
+  int rope;                  // 0 NeoX, 1 interleaved, 2 none
+  bool sanitize;             // rotated NaN -> +0
+  uint32_t ratio;            // compress ratio, >= 1
+  uint32_t ratio_magic;      // p / ratio == (umulhi(p, ratio_magic) + p) >> ratio_shift
+  uint32_t ratio_shift;      //   for every p < 2^31
+  uint32_t amax_floor_bits;  // fp32 bits of the amax floor (0 = none)
+};
+
+hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
+                         const int64_t *positions, const float *cos_sin, int64_t max_pos,
+                         bool legacy, const InsertOptions &o, hipStream_t stream);
 hipError_t launch_gather_mxfp8(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
                                hipStream_t stream);
 hipError_t launch_gather_legacy(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,

@@ -24,7 +24,7 @@ def workers() -> int:
 
 
 def oracle_insert(case: W.InsertCase, backing: np.ndarray, kv_bits=None, slots=None,
-                  positions=None, chunk: int = 8192) -> np.ndarray:
+                  positions=None, chunk: int = 8192, **opts) -> np.ndarray:
     kv = case.kv_bits if kv_bits is None else kv_bits
     sl = case.slot_mapping if slots is None else slots
     ps = case.positions if positions is None else positions
@@ -34,7 +34,7 @@ def oracle_insert(case: W.InsertCase, backing: np.ndarray, kv_bits=None, slots=N
     def run(ab):
         a, b = ab
         oracle.insert(kv[a:b], backing, case.num_blocks, case.page_stride, case.block_size,
-                      case.record, sl[a:b], ps[a:b], case.cos_sin)
+                      case.record, sl[a:b], ps[a:b], case.cos_sin, **opts)
 
     if len(jobs) <= 1:
         for j in jobs:
@@ -86,11 +86,11 @@ class DeviceCase:
         self.backing, self.k_cache = B.alloc_cache(case.num_blocks, case.block_size, case.record,
                                                    case.page_stride, backing=dev(init, device))
 
-    def insert(self, kv=None, slots=None, positions=None):
+    def insert(self, kv=None, slots=None, positions=None, **opts):
         B.kvrec_insert(self.kv if kv is None else kv, self.k_cache,
                        self.slots if slots is None else slots,
                        self.positions if positions is None else positions,
-                       self.cos_sin, self.case.block_size)
+                       self.cos_sin, self.case.block_size, **opts)
 
     def gather(self, indices: np.ndarray) -> np.ndarray:
         out = B.kvrec_gather(self.k_cache, dev(np.ascontiguousarray(indices, np.int32)))

@@ -21,7 +21,7 @@ from quantized_paged_kv_rope_amd import build as KB
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvrec.h")
 
-OK, NULL, RECORD, BLOCK, STRIDE, ALIGN, SIZE = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, RECORD, BLOCK, STRIDE, ALIGN, SIZE, OPTION = 0, -1, -2, -3, -4, -5, -6, -8
 FAKE = 0x10000  # aligned, never dereferenced
 
 
@@ -66,7 +66,7 @@ def test_library_does_not_depend_on_the_oracle():
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, RECORD, BLOCK, STRIDE, ALIGN, SIZE, -7, 12345):
+    for code in (OK, NULL, RECORD, BLOCK, STRIDE, ALIGN, SIZE, -7, OPTION, 12345):
         s = lib.kvrec_status_str(code)
         assert s and isinstance(s, bytes)
     assert lib.kvrec_status_str(OK) == b"ok"
@@ -152,6 +152,33 @@ def test_gather_validation(lib):
     assert gat(lib, good, out=FAKE + 8) == ALIGN
     assert gat(lib, good, idx=FAKE + 2) == ALIGN
     assert gat(lib, cache(base=FAKE + 1)) == ALIGN
+
+
+def ins_ex(lib, c, opts, n=8, kv=FAKE, slots=FAKE, pos=FAKE, cs=FAKE, max_pos=16, bs=64, rec=528):
+    return lib.kvrec_insert_ex(kv, n, ctypes.byref(c), slots, pos, cs, max_pos, bs, rec,
+                               ctypes.byref(opts) if opts is not None else None, None)
+
+
+def test_insert_options_validation(lib):
+    good = cache()
+    O = B.kvrec_insert_options
+    assert ins_ex(lib, good, None, n=0) == OK
+    assert ins_ex(lib, good, O(1, 4, 1e-4, 1), n=0) == OK
+    assert ins_ex(lib, good, O(3, 1, 0.0, 0)) == OPTION       # unknown rotation
+    assert ins_ex(lib, good, O(-1, 1, 0.0, 0)) == OPTION
+    assert ins_ex(lib, good, O(1, 0, 0.0, 0)) == OPTION       # ratio < 1
+    assert ins_ex(lib, good, O(1, 2 ** 30 + 1, 0.0, 0)) == OPTION
+    assert ins_ex(lib, good, O(1, 1, -1e-4, 0)) == OPTION     # negative floor
+    assert ins_ex(lib, good, O(1, 1, float("nan"), 0)) == OPTION
+    assert ins_ex(lib, good, O(1, 1, float("inf"), 0)) == OPTION
+    assert ins_ex(lib, good, O(1, 1, 0.0, 2)) == OPTION       # sanitize is 0 or 1
+    # what may be NULL: the table without a rotation; positions too with ratio 1
+    assert ins_ex(lib, good, O(0, 1, 0.0, 0), pos=None) == NULL
+    assert ins_ex(lib, good, O(1, 1, 0.0, 0), cs=None) == NULL
+    assert ins_ex(lib, good, O(2, 2, 0.0, 0), pos=None) == NULL  # the ratio gate needs them
+    assert ins_ex(lib, good, O(2, 1, 0.0, 0), n=0, pos=None, cs=None) == OK
+    assert ins_ex(lib, good, O(0, 1, 0.0, 0), max_pos=2 ** 30 + 1) == SIZE
+    assert lib.kvrec_status_str(OPTION) == b"insert option out of range"
 
 
 def test_legacy_cache_accepted(lib):
