@@ -152,6 +152,22 @@ def all_configs_report(dev, out=sys.stderr) -> list:
         ib = valid * (1024 + 8 + 8 + 256 + case.record) + (n - valid) * 8
         add(case.name, f"insert {case.record} B", n, valid, ib,
             lambda: B.kvrec_insert(kv, kc, sl, ps, cs, case.block_size))
+        if case.name.startswith("prefill"):
+            # the compressed-KV insert: gated tokens read slot + position only
+            p1 = case.positions[:n] + 1
+            for ratio in (1, 4):
+                keep = (case.slot_mapping >= 0) & (p1 % ratio == 0) & (p1 >= ratio)
+                kept = int(keep.sum())
+                vb = kept * (1024 + 8 + 8 + 256 + case.record) + (valid - kept) * 16 + \
+                    (n - valid) * 8
+                add(case.name, f"cmp r{ratio} {case.record}", n, kept, vb,
+                    lambda r=ratio: B.kvrec_insert(kv, kc, sl, ps, cs, case.block_size,
+                                                   rope="interleaved", compress_ratio=r,
+                                                   amax_floor=1e-4, sanitize_nans=True))
+            nb = valid * (1024 + 8 + case.record) + (n - valid) * 8
+            add(case.name, f"norope {case.record}", n, valid, nb,
+                lambda: B.kvrec_insert_ex(kv, kc, sl, None, None, case.block_size,
+                                          options=B.insert_options(rope="none")))
         if case.name.startswith("decode"):
             continue
         idx = up(case.gather_indices)

@@ -22,6 +22,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 HEAD_DIM = 512
 RECORD_MXFP8 = 528
 RECORD_LEGACY = 584
+RECORD_BF16 = 1024
+RECORD_FP8 = 512
 
 _lib = None
 
@@ -91,6 +93,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_insert_ex.restype = ctypes.c_int
     L.orc_rope_rows_ex.argtypes = [p, i64, p, p, ctypes.POINTER(InsertOptions), p]
     L.orc_rope_rows_ex.restype = None
+    L.orc_insert_full.argtypes = [p, i64, p, i64, i64, i32, i32, p, p, p, i64, ctypes.c_float]
+    L.orc_insert_full.restype = ctypes.c_int
     L.orc_gather.argtypes = [p, i64, i64, i32, i32, p, i64, p]
     L.orc_gather.restype = ctypes.c_int
     L.orc_e4m3_encode_f32.argtypes = [p, i64, p]
@@ -247,6 +251,33 @@ def insert(kv_bits: np.ndarray, backing: np.ndarray, num_blocks: int, page_strid
                               _ptr(cos_sin), cos_sin.shape[0])
     if rc != 0:
         raise ValueError(f"oracle insert rejected record={record} options={opts}")
+
+
+def insert_full(kv_bits: np.ndarray, backing: np.ndarray, num_blocks: int, page_stride: int,
+                block_size: int, record: int, slot_mapping: np.ndarray, positions: np.ndarray,
+                cos_sin: np.ndarray, fp8_scale: float = 1.0) -> None:
+    """Insert into a non-packed cache (record 1024 = bf16, 512 = fp8 e4m3fn
+    with the per-tensor ``fp8_scale``), in place in ``backing``."""
+    kv_bits = _c(kv_bits, np.uint16)
+    slot_mapping = _c(slot_mapping, np.int64)
+    positions = _c(positions, np.int64)
+    cos_sin = _c(cos_sin, np.float32)
+    if backing.dtype != np.uint8 or not backing.flags.c_contiguous:
+        raise TypeError("backing must be a contiguous uint8 array")
+    n = slot_mapping.shape[0]
+    if kv_bits.ndim != 2 or kv_bits.shape[1] != HEAD_DIM or kv_bits.shape[0] < n:
+        raise ValueError("kv must be [>=n, 512]")
+    if positions.shape[0] < n:
+        raise ValueError("positions must cover every token")
+    if cos_sin.ndim != 2 or cos_sin.shape[1] != 64:
+        raise ValueError("cos_sin_cache must be [max_pos, 64]")
+    if backing.size < (num_blocks - 1) * page_stride + block_size * record and num_blocks > 0:
+        raise ValueError("backing too small for the cache geometry")
+    rc = lib().orc_insert_full(_ptr(kv_bits), n, _ptr(backing), num_blocks, page_stride,
+                               block_size, record, _ptr(slot_mapping), _ptr(positions),
+                               _ptr(cos_sin), cos_sin.shape[0], float(fp8_scale))
+    if rc != 0:
+        raise ValueError(f"oracle full-cache insert rejected record={record}")
 
 
 def gather(backing: np.ndarray, num_blocks: int, page_stride: int, block_size: int,

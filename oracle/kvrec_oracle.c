@@ -314,6 +314,53 @@ int orc_insert_ex(const uint16_t *kv, int64_t n, uint8_t *cache, int64_t num_blo
 }
 
 /* ------------------------------------------------------------------------ */
+/* Non-packed caches of the KV-only op [KV-only op, 实现拆解 1]: the same    */
+/* skip and NeoX rotation, then a plain row of 512 elements per slot at      */
+/* page + off * record, with no scale region:                               */
+/*   record 1024, bf16 cache: element d is bf16_RNE(r[d]) (dims 0..447 are   */
+/*     the input bits unchanged, since r[d] is their exact widening);        */
+/*   record 512, fp8 e4m3fn cache with one fp32 per-tensor scale s: element  */
+/*     d is the e4m3fn code nearest to the binary32 quotient fl(r[d] / s),   */
+/*     saturated to +-448 (a reading: the page requires the fp32 scale but   */
+/*     does not print the step; dividing by the scale makes code * s the     */
+/*     stored value, and the quotient is formed in fp32, the op's type).     */
+/* ------------------------------------------------------------------------ */
+int orc_insert_full(const uint16_t *kv, int64_t n, uint8_t *cache, int64_t num_blocks,
+                    int64_t page_stride, int32_t block_size, int32_t record,
+                    const int64_t *slot_mapping, const int64_t *positions,
+                    const float *cos_sin_cache, int64_t max_pos, float fp8_scale) {
+  int64_t t;
+  int64_t total_slots = num_blocks * (int64_t)block_size;
+  if (record != ORC_RECORD_BF16 && record != ORC_RECORD_FP8) return -1;
+
+  for (t = 0; t < n; ++t) {
+    float r[HEAD_DIM];
+    int64_t slot = slot_mapping[t];
+    int64_t pos = positions[t];
+    uint8_t *row;
+    int d;
+
+    if (slot < 0 || slot >= total_slots) continue;
+    if (pos < 0 || pos >= max_pos) continue;
+    rope_row(kv + t * HEAD_DIM, cos_sin_cache + pos * ROPE_DIM, r);
+    row = cache + (slot / block_size) * page_stride + (slot % block_size) * record;
+    if (record == ORC_RECORD_BF16) {
+      for (d = 0; d < HEAD_DIM; ++d) {
+        uint16_t h = orc_bf16_round((double)r[d]);
+        row[2 * d] = (uint8_t)(h & 0xFF);
+        row[2 * d + 1] = (uint8_t)(h >> 8);
+      }
+    } else {
+      for (d = 0; d < HEAD_DIM; ++d) {
+        float y = r[d] / fp8_scale;
+        row[d] = orc_e4m3_encode((double)y);
+      }
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Gather (dequantise to bf16). Index = page * block_size + offset; a       */
 /* negative index marks an invalid entry [FlashMLA, sparse decode           */
 /* integration notes] and yields a row of +0. Reading: an index >=          */

@@ -40,7 +40,7 @@ uint16_t orc_bf16_round(double x);
  * amax == 0 gives 0. */
 int orc_scale_exponent(float amax);
 
-/* ---- the two operations ------------------------------------------------ */
+/* ---- the operations ---------------------------------------------------- */
 
 /* Insert n tokens into a host copy of the paged cache.
  *   kv            bf16 bits [n, 512], row-major
@@ -74,6 +74,18 @@ int orc_insert_ex(const uint16_t *kv, int64_t n, uint8_t *cache, int64_t num_blo
                   const int64_t *slot_mapping, const int64_t *positions,
                   const float *cos_sin_cache, int64_t max_pos,
                   const orc_insert_options *opts);
+
+/* Non-packed caches [KV-only op, 实现拆解 1]: record = bytes per slot.
+ *   ORC_RECORD_BF16  512 bf16 elements, little-endian
+ *   ORC_RECORD_FP8   512 e4m3fn codes of fl(r / fp8_scale), saturated
+ * Rows sit at page * page_stride + (slot % block_size) * record; there is no
+ * scale region. The rotation is the NeoX one of orc_insert; fp8_scale is
+ * read only for ORC_RECORD_FP8. Returns 0, or -1 for another record. */
+enum { ORC_RECORD_BF16 = 1024, ORC_RECORD_FP8 = 512 };
+int orc_insert_full(const uint16_t *kv, int64_t n, uint8_t *cache, int64_t num_blocks,
+                    int64_t page_stride, int32_t block_size, int32_t record,
+                    const int64_t *slot_mapping, const int64_t *positions,
+                    const float *cos_sin_cache, int64_t max_pos, float fp8_scale);
 
 /* Gather n records back to bf16 rows.
  *   token_indices [n] int32, page * block_size + offset; negative -> zeros

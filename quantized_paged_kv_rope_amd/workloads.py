@@ -33,13 +33,16 @@ HEAD_DIM = 512
 ROPE_DIM = 64
 RECORD_MXFP8 = 528
 RECORD_LEGACY = 584
+RECORD_BF16 = 1024  # non-packed bf16 cache: 512 elements per slot
+RECORD_FP8 = 512    # non-packed e4m3fn cache with a per-tensor scale
 ROPE_THETA = 10000.0
 
 
 def page_stride_for(record: int, block_size: int) -> int:
     """Smallest multiple of the record's page alignment (512 B for the MXFP8
-    record, 576 B for the legacy one) that holds ``block_size`` records."""
-    align = 512 if record == RECORD_MXFP8 else 576
+    record, 576 B for the legacy one, 16 B for the non-packed rows) that
+    holds ``block_size`` records."""
+    align = {RECORD_MXFP8: 512, RECORD_LEGACY: 576}.get(record, 16)
     raw = block_size * record
     return (raw + align - 1) // align * align
 
