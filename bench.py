@@ -168,6 +168,16 @@ def all_configs_report(dev, out=sys.stderr) -> list:
             add(case.name, f"norope {case.record}", n, valid, nb,
                 lambda: B.kvrec_insert_ex(kv, kc, sl, None, None, case.block_size,
                                           options=B.insert_options(rope="none")))
+            # the non-packed caches: bf16 rows and per-tensor-scaled fp8 rows
+            for rec in (B.RECORD_BF16, B.RECORD_FP8):
+                fb, fc = B.alloc_cache(case.num_blocks, case.block_size, rec, device=dev)
+                sc = torch.tensor([0.0625], dtype=torch.float32, device=dev) \
+                    if rec == B.RECORD_FP8 else None
+                fbytes = valid * (1024 + 8 + 8 + 256 + rec) + (n - valid) * 8
+                add(case.name, f"full {rec} B", n, valid, fbytes,
+                    lambda fc=fc, sc=sc: B.kvrec_insert_full(kv, fc, sl, ps, cs,
+                                                             case.block_size, sc))
+                del fb, fc
         if case.name.startswith("decode"):
             continue
         idx = up(case.gather_indices)

@@ -5,7 +5,9 @@
  * per token:
  *
  *   kvrec_insert  fused fp32 RoPE on the 64 tail dims + MXFP8 (or legacy)
- *                 quantisation + paged store of the token's record;
+ *                 quantisation + paged store of the token's record
+ *                 (kvrec_insert_ex adds the compressed-KV options;
+ *                 kvrec_insert_full writes the non-packed bf16 / fp8 caches);
  *   kvrec_gather  the inverse: paged read + dequantisation to bf16 rows.
  *
  * Sources (page titles; sections named as on the pages):
@@ -57,11 +59,25 @@ extern "C" {
 #define KVREC_RECORD_MXFP8 528
 #define KVREC_RECORD_LEGACY 584
 
+/* Non-packed caches of the KV-only op ([KV-only op] 实现拆解 1: a bf16 cache,
+ * or an fp8 e4m3fn cache with one float32 per-tensor scale; 512 elements per
+ * token), written by kvrec_insert_full only. Widths in bytes per token:
+ *   1024  bf16 row: the 512 dims as bf16 (rotated tail rounded to nearest
+ *         even; dims 0..447 are the input bits).
+ *   512   fp8 row: the 512 dims as e4m3fn codes of the fp32 quotient
+ *         r / scale, nearest even, saturated to +-448.
+ * A slot's row sits at page + (slot % block_size) * width; there is no scale
+ * region. Page alignment 16 B. */
+#define KVREC_RECORD_BF16 1024
+#define KVREC_RECORD_FP8 512
+
 typedef enum kvrec_status {
   KVREC_OK = 0,
   KVREC_ERR_NULL = -1,        /* a required pointer is NULL               */
-  KVREC_ERR_RECORD = -2,      /* record not 528/584, or != cache's record */
-  KVREC_ERR_BLOCK_SIZE = -3,  /* block_size < 1, or != cache's block_size */
+  KVREC_ERR_RECORD = -2,      /* record not one the call takes, or !=
+                                 the cache's record                       */
+  KVREC_ERR_BLOCK_SIZE = -3,  /* block_size < 1, != cache's block_size, or
+                                 block_size * record > 2^31               */
   KVREC_ERR_PAGE_STRIDE = -4, /* page stride not a multiple of the record's
                                  alignment, or < block_size * record      */
   KVREC_ERR_ALIGNMENT = -5,   /* a pointer is not aligned as stated below */
@@ -76,22 +92,24 @@ typedef enum kvrec_status {
  * 576 B for the legacy record) followed by a scale region (block_size rows of
  * 16 B, or 8 B) and then padding up to page_stride ([MXFP8 record] 实现拆解 4
  * and 关键源码片段: data at page + off*512, scales at page + block*512 +
- * off*16). A token in slot s lives in page s / block_size at offset
- * s % block_size. */
+ * off*16). The non-packed caches have the data region only. A token in slot
+ * s lives in page s / block_size at offset s % block_size. */
 typedef struct kvrec_cache {
   void *base;          /* (device) byte 0 of page 0; 16-B aligned          */
   int64_t num_blocks;  /* pages, >= 0; num_blocks * block_size <= 2^30   */
-  int64_t page_stride; /* bytes between pages; a multiple of 512 (528) or
-                          576 (584) and >= block_size * record             */
-  int32_t block_size;  /* tokens per page, >= 1                            */
-  int32_t record;      /* 528 or 584                                       */
+  int64_t page_stride; /* bytes between pages; a multiple of 512 (528),
+                          576 (584) or 16 (1024, 512), and >= block_size *
+                          record                                           */
+  int32_t block_size;  /* tokens per page, >= 1; block_size * record
+                          <= 2^31                                          */
+  int32_t record;      /* 528, 584, 1024 or 512                            */
 } kvrec_cache;
 
 /* hipStream_t, passed opaquely so this header needs no HIP headers. */
 typedef void *kvrec_stream;
 
 /* Page stride for a record and block size: block_size * record rounded up
- * to the record's alignment (512 or 576). Host-only, pure.
+ * to the record's alignment (512, 576 or 16). Host-only, pure.
  * Returns KVREC_OK and writes *page_stride_out, or KVREC_ERR_NULL,
  * KVREC_ERR_RECORD, KVREC_ERR_BLOCK_SIZE. */
 int kvrec_page_stride(int32_t record, int32_t block_size, int64_t *page_stride_out);
@@ -170,6 +188,23 @@ int kvrec_insert_ex(const void *kv, int64_t num_tokens, const kvrec_cache *k_cac
                     const float *cos_sin_cache, int64_t max_pos, int32_t block_size,
                     int32_t record, const kvrec_insert_options *options,
                     kvrec_stream stream);
+
+/* Insert into a non-packed cache (record KVREC_RECORD_BF16 or
+ * KVREC_RECORD_FP8): the KV-only op's bf16 and fp8 branches ([KV-only op]
+ * 实现拆解 1, which requires a float32 scalar scale for the fp8 cache).
+ * Arguments, skip rules and errors as kvrec_insert, with the NeoX rotation
+ * and no options, plus:
+ *   fp8_scale  (device) one fp32, 4-B aligned, read on the device: the
+ *              per-tensor scale of the fp8 cache (stored code * scale
+ *              approximates the value). Required (KVREC_ERR_NULL) for
+ *              record 512; must be NULL (KVREC_ERR_OPTION) for record 1024.
+ *              The caller keeps it positive and finite.
+ * The packed calls (kvrec_insert, kvrec_insert_ex, kvrec_gather) refuse
+ * these records with KVREC_ERR_RECORD, and this call refuses 528 / 584. */
+int kvrec_insert_full(const void *kv, int64_t num_tokens, const kvrec_cache *k_cache,
+                      const int64_t *slot_mapping, const int64_t *positions,
+                      const float *cos_sin_cache, int64_t max_pos, int32_t block_size,
+                      int32_t record, const float *fp8_scale, kvrec_stream stream);
 
 /* Gather num_indices records back to bf16 rows ([MXFP8 record] 实现拆解 4:
  * one gather parameterised by the record; [FlashMLA]: index =

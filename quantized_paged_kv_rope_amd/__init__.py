@@ -1,5 +1,6 @@
 """MI355X (gfx950) paged KV-record codec: fused RoPE + MXFP8 quantise +
-paged insert, and the paged dequantise-and-gather, for 512-dim MLA latent KV.
+paged insert (also into plain bf16 and per-tensor-scaled fp8 caches), and the
+paged dequantise-and-gather, for 512-dim MLA latent KV.
 
 The compute lives in ``libkvrec.so`` (HIP kernels behind the C ABI of
 ``include/kvrec.h``); :mod:`.binding` marshals torch tensors into it. The
@@ -9,6 +10,8 @@ compute call fails loudly without them.
 """
 from .binding import (  # noqa: F401
     HEAD_DIM,
+    RECORD_BF16,
+    RECORD_FP8,
     RECORD_LEGACY,
     RECORD_MXFP8,
     ROPE_DIM,
@@ -19,6 +22,7 @@ from .binding import (  # noqa: F401
     insert_options,
     kvrec_insert,
     kvrec_insert_ex,
+    kvrec_insert_full,
     kvrec_insert_options,
     kvrec_page_stride,
     kvrec_status_str,

@@ -11,9 +11,13 @@ Shapes follow the page's KV-only op ([KV-only op] 实现拆解 1; page title
 * ``kv``             bf16 ``[tokens, 512]`` contiguous (not modified)
 * ``k_cache``        uint8 ``[num_blocks, block_size, record]`` with
                      ``stride(2) == 1`` and ``stride(1) == record``; the
-                     record (528 or 584) is read from the last dimension and
-                     the page stride from ``stride(0)`` (a padded stride is
-                     expressed with ``as_strided``; see :func:`alloc_cache`)
+                     record (528 or 584; 1024 or 512 for the non-packed
+                     caches) is read from the last dimension and the page
+                     stride from ``stride(0)`` (a padded stride is expressed
+                     with ``as_strided``; see :func:`alloc_cache`). The
+                     non-packed caches may also be given as a bf16 or
+                     float8_e4m3fn ``[num_blocks, block_size, 512]`` view,
+                     as the page's op takes them.
 * ``slot_mapping``   int64 ``[tokens]`` (token count = its length)
 * ``positions``      int64 covering every token
 * ``cos_sin_cache``  fp32 ``[max_pos, 64]`` (32 cos then 32 sin)
@@ -33,6 +37,8 @@ HEAD_DIM = 512
 ROPE_DIM = 64
 RECORD_MXFP8 = 528
 RECORD_LEGACY = 584
+RECORD_BF16 = 1024  # non-packed bf16 cache (512 elements per token)
+RECORD_FP8 = 512    # non-packed e4m3fn cache with a per-tensor fp32 scale
 MAX_POS = 1 << 30  # the C ABI's limit on table rows
 
 KVREC_OK = 0
@@ -41,8 +47,8 @@ STATUS_NAMES = {
     -4: "KVREC_ERR_PAGE_STRIDE", -5: "KVREC_ERR_ALIGNMENT", -6: "KVREC_ERR_SIZE",
     -7: "KVREC_ERR_HIP", -8: "KVREC_ERR_OPTION",
 }
-EXPORTED_SYMBOLS = ("kvrec_page_stride", "kvrec_insert", "kvrec_insert_ex", "kvrec_gather",
-                    "kvrec_status_str")
+EXPORTED_SYMBOLS = ("kvrec_page_stride", "kvrec_insert", "kvrec_insert_ex", "kvrec_insert_full",
+                    "kvrec_gather", "kvrec_status_str")
 ROPE = {"neox": 0, "interleaved": 1, "none": 2}
 
 
@@ -106,6 +112,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvrec_insert_ex.argtypes = [p, i64, ctypes.POINTER(kvrec_cache), p, p, p, i64, i32, i32,
                                   ctypes.POINTER(kvrec_insert_options), p]
     L.kvrec_insert_ex.restype = ctypes.c_int
+    L.kvrec_insert_full.argtypes = [p, i64, ctypes.POINTER(kvrec_cache), p, p, p, i64, i32, i32,
+                                    p, p]
+    L.kvrec_insert_full.restype = ctypes.c_int
     L.kvrec_gather.argtypes = [ctypes.POINTER(kvrec_cache), p, i64, p, p]
     L.kvrec_gather.restype = ctypes.c_int
     L.kvrec_status_str.argtypes = [ctypes.c_int]
@@ -136,16 +145,29 @@ def _require_gpu(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be on a GPU (got {t.device})")
 
 
+_ELEMENT_CACHES = {torch.bfloat16: RECORD_BF16, torch.float8_e4m3fn: RECORD_FP8}
+
+
 def cache_descriptor(k_cache: torch.Tensor) -> kvrec_cache:
-    """The C descriptor of a ``[num_blocks, block_size, record]`` uint8 view."""
+    """The C descriptor of a ``[num_blocks, block_size, record]`` uint8 view,
+    or of a bf16 / float8_e4m3fn ``[num_blocks, block_size, 512]`` view of a
+    non-packed cache (record 1024 / 512 bytes)."""
     _require_gpu(k_cache, "k_cache")
-    if k_cache.dtype != torch.uint8 or k_cache.dim() != 3:
-        raise TypeError("k_cache must be a 3-D uint8 tensor [num_blocks, block_size, record]")
-    nb, bs, rec = k_cache.shape
-    if k_cache.stride(2) != 1 or (bs > 1 and k_cache.stride(1) != rec):
-        raise ValueError("k_cache must have stride(2) == 1 and stride(1) == record")
-    stride0 = k_cache.stride(0) if nb > 1 else kvrec_page_stride(rec, bs) if rec in (
-        RECORD_MXFP8, RECORD_LEGACY) else bs * rec
+    if k_cache.dim() != 3 or (k_cache.dtype != torch.uint8 and
+                              k_cache.dtype not in _ELEMENT_CACHES):
+        raise TypeError("k_cache must be a 3-D uint8 tensor [num_blocks, block_size, record], "
+                        "or a bf16 / float8_e4m3fn [num_blocks, block_size, 512] view")
+    nb, bs, width = k_cache.shape
+    if k_cache.stride(2) != 1 or (bs > 1 and k_cache.stride(1) != width):
+        raise ValueError("k_cache must have stride(2) == 1 and stride(1) == its last dimension")
+    item = k_cache.element_size()
+    if k_cache.dtype == torch.uint8:
+        rec = width
+    elif width != HEAD_DIM:
+        raise ValueError("a bf16 / fp8 k_cache view must be [num_blocks, block_size, 512]")
+    else:
+        rec = _ELEMENT_CACHES[k_cache.dtype]
+    stride0 = k_cache.stride(0) * item if nb > 1 else kvrec_page_stride(rec, bs)
     return kvrec_cache(k_cache.data_ptr(), nb, stride0, bs, rec)
 
 
@@ -170,12 +192,7 @@ def kvrec_insert(kv: torch.Tensor, k_cache: torch.Tensor, slot_mapping: torch.Te
                     None if default else opts)
 
 
-def kvrec_insert_ex(kv: torch.Tensor, k_cache: torch.Tensor, slot_mapping: torch.Tensor,
-                    positions: Optional[torch.Tensor], cos_sin_cache: Optional[torch.Tensor],
-                    block_size: int, record: Optional[int] = None,
-                    options: Optional[kvrec_insert_options] = None) -> None:
-    """The C ``kvrec_insert_ex``: :func:`kvrec_insert` with an options struct
-    (``None`` = the defaults, which calls the C ``kvrec_insert``)."""
+def _check_insert_inputs(kv, k_cache, slot_mapping, positions, cos_sin_cache) -> list:
     tensors = [("kv", kv), ("slot_mapping", slot_mapping)]
     if positions is not None:
         tensors.append(("positions", positions))
@@ -201,8 +218,19 @@ def kvrec_insert_ex(kv: torch.Tensor, k_cache: torch.Tensor, slot_mapping: torch
     devs = {t.device for _, t in tensors} | {k_cache.device}
     if len(devs) != 1:
         raise ValueError(f"all tensors must be on one device, got {devs}")
+    return tensors
+
+
+def kvrec_insert_ex(kv: torch.Tensor, k_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                    positions: Optional[torch.Tensor], cos_sin_cache: Optional[torch.Tensor],
+                    block_size: int, record: Optional[int] = None,
+                    options: Optional[kvrec_insert_options] = None) -> None:
+    """The C ``kvrec_insert_ex``: :func:`kvrec_insert` with an options struct
+    (``None`` = the defaults, which calls the C ``kvrec_insert``)."""
+    _check_insert_inputs(kv, k_cache, slot_mapping, positions, cos_sin_cache)
+    n = slot_mapping.shape[0]
     desc = cache_descriptor(k_cache)
-    rec = int(k_cache.shape[2]) if record is None else int(record)
+    rec = desc.record if record is None else int(record)
     pos_p = positions.data_ptr() if positions is not None else None
     cs_p = cos_sin_cache.data_ptr() if cos_sin_cache is not None else None
     # Without a table (rotation-free insert) positions only feed the ratio
@@ -217,6 +245,35 @@ def kvrec_insert_ex(kv: torch.Tensor, k_cache: torch.Tensor, slot_mapping: torch
             _check(load_library().kvrec_insert_ex(
                 kv.data_ptr(), n, ctypes.byref(desc), slot_mapping.data_ptr(), pos_p, cs_p,
                 max_pos, int(block_size), rec, ctypes.byref(options), _stream_handle(kv.device)))
+
+
+def kvrec_insert_full(kv: torch.Tensor, k_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                      positions: torch.Tensor, cos_sin_cache: torch.Tensor, block_size: int,
+                      fp8_scale: Optional[torch.Tensor] = None,
+                      record: Optional[int] = None) -> None:
+    """The C ``kvrec_insert_full``: RoPE + insert into a non-packed cache
+    ([KV-only op] 实现拆解 1): bf16 rows (record 1024) or e4m3fn rows of
+    ``r / fp8_scale`` (record 512; ``fp8_scale`` a one-element fp32 GPU
+    tensor, required there and refused for bf16)."""
+    if positions is None or cos_sin_cache is None:
+        raise ValueError("the non-packed insert rotates: positions and cos_sin_cache are needed")
+    _check_insert_inputs(kv, k_cache, slot_mapping, positions, cos_sin_cache)
+    n = slot_mapping.shape[0]
+    desc = cache_descriptor(k_cache)
+    rec = desc.record if record is None else int(record)
+    scale_p = None
+    if fp8_scale is not None:
+        _require_gpu(fp8_scale, "fp8_scale")
+        if fp8_scale.dtype != torch.float32 or fp8_scale.numel() != 1:
+            raise TypeError("fp8_scale must be a one-element fp32 tensor")
+        if fp8_scale.device != kv.device:
+            raise ValueError("fp8_scale must be on kv's device")
+        scale_p = fp8_scale.data_ptr()
+    with torch.cuda.device(kv.device):
+        _check(load_library().kvrec_insert_full(
+            kv.data_ptr(), n, ctypes.byref(desc), slot_mapping.data_ptr(), positions.data_ptr(),
+            cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], int(block_size), rec, scale_p,
+            _stream_handle(kv.device)))
 
 
 def kvrec_gather(k_cache: torch.Tensor, token_indices: torch.Tensor,

@@ -6,7 +6,9 @@
 // nothing runs on failure), restated for plain pointers: the record width
 // selects the kernel, the block size is cross-checked against the cache, the
 // page stride must be a multiple of the record's page alignment (512 B for
-// the 528 B record, 576 B for the 584 B record: [MXFP8 record] 功能与动机).
+// the 528 B record, 576 B for the 584 B record: [MXFP8 record] 功能与动机;
+// 16 B, the width of one vector store, for the non-packed rows), and the fp8
+// cache needs its scale.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -25,11 +27,23 @@ bool misaligned(const void *p, uintptr_t align) {
   return (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0;
 }
 
-int64_t record_alignment(int32_t record) { return record == KVREC_RECORD_MXFP8 ? 512 : 576; }
+int64_t record_alignment(int32_t record) {
+  return record == KVREC_RECORD_MXFP8 ? 512 : record == KVREC_RECORD_LEGACY ? 576 : 16;
+}
 
-bool known_record(int32_t record) {
+bool packed_record(int32_t record) {
   return record == KVREC_RECORD_MXFP8 || record == KVREC_RECORD_LEGACY;
 }
+
+bool full_record(int32_t record) {
+  return record == KVREC_RECORD_BF16 || record == KVREC_RECORD_FP8;
+}
+
+bool known_record(int32_t record) { return packed_record(record) || full_record(record); }
+
+// In-page byte offsets are computed in 32 bits on the device; a page of
+// block_size records must stay below 2^31 bytes.
+constexpr int64_t kMaxPageBytes = int64_t{1} << 31;
 
 // Division by an invariant block size with a multiply-high (Granlund and
 // Montgomery, "Division by invariant integers using multiplication", 1994):
@@ -50,6 +64,7 @@ int check_cache(const kvrec_cache *c, kvrec::CacheGeom *g) {
   if (c->block_size < 1) return KVREC_ERR_BLOCK_SIZE;
   if (c->num_blocks < 0) return KVREC_ERR_SIZE;
   const int64_t page_bytes = static_cast<int64_t>(c->block_size) * c->record;
+  if (page_bytes > kMaxPageBytes) return KVREC_ERR_BLOCK_SIZE;
   if (c->page_stride < page_bytes || c->page_stride % record_alignment(c->record) != 0)
     return KVREC_ERR_PAGE_STRIDE;
   if (c->num_blocks > kMaxCount / c->block_size) return KVREC_ERR_SIZE;
@@ -70,7 +85,8 @@ extern "C" {
 int kvrec_page_stride(int32_t record, int32_t block_size, int64_t *page_stride_out) {
   if (page_stride_out == nullptr) return KVREC_ERR_NULL;
   if (!known_record(record)) return KVREC_ERR_RECORD;
-  if (block_size < 1) return KVREC_ERR_BLOCK_SIZE;
+  if (block_size < 1 || static_cast<int64_t>(block_size) * record > kMaxPageBytes)
+    return KVREC_ERR_BLOCK_SIZE;
   const int64_t align = record_alignment(record);
   const int64_t raw = static_cast<int64_t>(block_size) * record;
   *page_stride_out = (raw + align - 1) / align * align;
@@ -90,7 +106,7 @@ int kvrec_insert_ex(const void *kv, int64_t num_tokens, const kvrec_cache *k_cac
                     const float *cos_sin_cache, int64_t max_pos, int32_t block_size,
                     int32_t record, const kvrec_insert_options *options, kvrec_stream stream) {
   if (k_cache == nullptr) return KVREC_ERR_NULL;
-  if (!known_record(record) || record != k_cache->record) return KVREC_ERR_RECORD;
+  if (!packed_record(record) || record != k_cache->record) return KVREC_ERR_RECORD;
   if (block_size < 1 || block_size != k_cache->block_size) return KVREC_ERR_BLOCK_SIZE;
   kvrec::CacheGeom g;
   const int rc = check_cache(k_cache, &g);
@@ -125,9 +141,48 @@ int kvrec_insert_ex(const void *kv, int64_t num_tokens, const kvrec_cache *k_cac
   const int64_t *pos = needs_positions ? positions : nullptr;
   if (pos == nullptr) max_pos = 1;
   if (!needs_table) cos_sin_cache = nullptr;
+  const kvrec::Format format =
+      record == KVREC_RECORD_LEGACY ? kvrec::Format::kLegacy : kvrec::Format::kMxfp8;
   const hipError_t err =
-      kvrec::launch_insert(kv, num_tokens, g, slot_mapping, pos, cos_sin_cache, max_pos,
-                           record == KVREC_RECORD_LEGACY, o, static_cast<hipStream_t>(stream));
+      kvrec::launch_insert(kv, num_tokens, g, slot_mapping, pos, cos_sin_cache, max_pos, format, o,
+                           nullptr, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? KVREC_OK : KVREC_ERR_HIP;
+}
+
+int kvrec_insert_full(const void *kv, int64_t num_tokens, const kvrec_cache *k_cache,
+                      const int64_t *slot_mapping, const int64_t *positions,
+                      const float *cos_sin_cache, int64_t max_pos, int32_t block_size,
+                      int32_t record, const float *fp8_scale, kvrec_stream stream) {
+  if (k_cache == nullptr) return KVREC_ERR_NULL;
+  if (!full_record(record) || record != k_cache->record) return KVREC_ERR_RECORD;
+  if (block_size < 1 || block_size != k_cache->block_size) return KVREC_ERR_BLOCK_SIZE;
+  kvrec::CacheGeom g;
+  const int rc = check_cache(k_cache, &g);
+  if (rc != KVREC_OK) return rc;
+  // The fp8 cache needs its scale ([KV-only op] 实现拆解 1); a scale given
+  // for the bf16 cache would be ignored, so it is refused instead.
+  if (record == KVREC_RECORD_FP8 && fp8_scale == nullptr) return KVREC_ERR_NULL;
+  if (record == KVREC_RECORD_BF16 && fp8_scale != nullptr) return KVREC_ERR_OPTION;
+  if (num_tokens < 0 || num_tokens > kMaxCount) return KVREC_ERR_SIZE;
+  if (num_tokens == 0) return KVREC_OK;
+  if (kv == nullptr || slot_mapping == nullptr || positions == nullptr ||
+      cos_sin_cache == nullptr)
+    return KVREC_ERR_NULL;
+  if (max_pos < 1 || max_pos > kMaxPos) return KVREC_ERR_SIZE;
+  if (misaligned(kv, 16) || misaligned(cos_sin_cache, 16) || misaligned(slot_mapping, 8) ||
+      misaligned(positions, 8) || misaligned(fp8_scale, 4))
+    return KVREC_ERR_ALIGNMENT;
+  kvrec::InsertOptions o;
+  o.rope = KVREC_ROPE_NEOX;
+  o.sanitize = false;
+  o.ratio = 1;
+  division_magic(1, &o.ratio_magic, &o.ratio_shift);
+  o.amax_floor_bits = 0;
+  const kvrec::Format format =
+      record == KVREC_RECORD_BF16 ? kvrec::Format::kBf16 : kvrec::Format::kFp8;
+  const hipError_t err =
+      kvrec::launch_insert(kv, num_tokens, g, slot_mapping, positions, cos_sin_cache, max_pos,
+                           format, o, fp8_scale, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? KVREC_OK : KVREC_ERR_HIP;
 }
 
@@ -136,6 +191,7 @@ int kvrec_gather(const kvrec_cache *k_cache, const int32_t *token_indices, int64
   kvrec::CacheGeom g;
   const int rc = check_cache(k_cache, &g);
   if (rc != KVREC_OK) return rc;
+  if (!packed_record(k_cache->record)) return KVREC_ERR_RECORD;
   if (num_indices < 0 || num_indices > kMaxCount) return KVREC_ERR_SIZE;
   if (num_indices == 0) return KVREC_OK;
   if (token_indices == nullptr || out == nullptr) return KVREC_ERR_NULL;
@@ -151,8 +207,11 @@ const char *kvrec_status_str(int status) {
   switch (status) {
     case KVREC_OK: return "ok";
     case KVREC_ERR_NULL: return "null pointer";
-    case KVREC_ERR_RECORD: return "record width is not 528 or 584, or does not match the cache";
-    case KVREC_ERR_BLOCK_SIZE: return "block_size < 1 or does not match the cache";
+    case KVREC_ERR_RECORD:
+      return "record width is not one this call takes (528/584 packed, 1024/512 non-packed), "
+             "or does not match the cache";
+    case KVREC_ERR_BLOCK_SIZE:
+      return "block_size < 1, does not match the cache, or makes a page of 2^31 bytes or more";
     case KVREC_ERR_PAGE_STRIDE:
       return "page stride is not a multiple of the record's page alignment or is too small";
     case KVREC_ERR_ALIGNMENT: return "pointer not aligned as the ABI requires";

@@ -1,6 +1,7 @@
 // kvrec_kernels.hip - gfx950 (MI355X, CDNA4) kernels of the paged KV-record
-// codec: fused RoPE + MXFP8 (or legacy) quantise + paged insert, and the
-// paged dequantise-and-gather.
+// codec: fused RoPE + MXFP8 (or legacy) quantise + paged insert, the same
+// insert into the non-packed bf16 and fp8 caches, and the paged
+// dequantise-and-gather.
 //
 // Sources (page titles; sections as named on the pages):
 //   [MXFP8 record] vLLM PR #56893 report, "[Model][DSv4.1] Store the whole KV
@@ -257,6 +258,12 @@ __device__ __forceinline__ void rope_tail(float f[8], const u32x4 raw, int lane,
 // 关键源码片段), or none (the K insert without RoPE).
 enum : int { kRopeNeox = 0, kRopeInterleaved = 1, kRopeNone = 2 };
 
+// Cache formats of the insert (kvrec::Format).
+constexpr int kFmtMxfp8 = static_cast<int>(Format::kMxfp8);
+constexpr int kFmtLegacy = static_cast<int>(Format::kLegacy);
+constexpr int kFmtBf16 = static_cast<int>(Format::kBf16);
+constexpr int kFmtFp8 = static_cast<int>(Format::kFp8);
+
 // Neighbour-pair rotation. Lane l holds pairs 4l..4l+3 (dims 8l..8l+7), so
 // no lane exchange is needed. As in the excerpt, the NoPE pairs (lanes < 56)
 // go through the same products with (cos, sin) = (1, 0); lane 56+j uses cos
@@ -279,11 +286,12 @@ __device__ __forceinline__ void rope_interleaved(float f[8], int lane, const f32
 
 // Encode one loaded token and store its record. `raw` is the lane's 16 B of
 // the bf16 row, c0..s1 the lane's cos/sin values (lanes 56..63 only).
-template <int P, bool kLegacy, int kRope, bool kSanitize, bool kOptions>
+template <int P, int kFmt, int kRope, bool kSanitize, bool kOptions>
 __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, const u32x4 raw,
                                              const f32x4 c0, const f32x4 c1, const f32x4 s0,
                                              const f32x4 s1, uint32_t slot,
-                                             uint32_t amax_floor_bits) {
+                                             uint32_t amax_floor_bits, float fp8_scale) {
+  constexpr bool kLegacy = kFmt == kFmtLegacy;
   float f[8];
   unpack_bf16x8(raw, f);
   if constexpr (kRope == kRopeNeox) rope_tail(f, raw, lane, c0, c1, s0, s1);
@@ -297,6 +305,32 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
   uint8_t *page = a.base + static_cast<int64_t>(po.page) * a.page_stride;
   constexpr bool nt_data = (P & kNtData) != 0;
   constexpr bool nt_scale = (P & kNtScale) != 0;
+
+  if constexpr (kFmt == kFmtBf16) {
+    // Non-packed bf16 cache ([KV-only op] 实现拆解 1): the 1 KB row at
+    // page + off*1024. The NoPE lanes store their input bits unchanged (the
+    // exact bf16 of an exact widening); the tail lanes round the rotation.
+    u32x4 h = raw;
+    if (lane >= 56) {
+      h.x = pack_bf16x2(f[0], f[1]);
+      h.y = pack_bf16x2(f[2], f[3]);
+      h.z = pack_bf16x2(f[4], f[5]);
+      h.w = pack_bf16x2(f[6], f[7]);
+    }
+    st<nt_data>(reinterpret_cast<u32x4 *>(page + off * 1024u + lane * 16), h);
+    return;
+  }
+  if constexpr (kFmt == kFmtFp8) {
+    // Non-packed fp8 cache with one fp32 per-tensor scale: the 512 B row at
+    // page + off*512 holds e4m3fn(r / scale), saturated to +-448. The
+    // quotient is one IEEE fp32 division (rounded once); the conversion then
+    // runs with a unit scale (UE8M0 byte 127 = 2^0), rounding to nearest even.
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = fminf(fmaxf(__fdiv_rn(f[k], fp8_scale), -448.0f), 448.0f);
+    st<nt_data>(reinterpret_cast<u32x2 *>(page + off * 512u + lane * 8), encode_e4m3x8(y, 127u));
+    return;
+  }
 
   uint32_t amax = lane_amax_bits(f);
   amax = dpp_umax<kQuadXor1>(amax);
@@ -359,19 +393,27 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
 // saves each wave a dependent kernarg load before its first memory request.
 // kOptions = false is the plain insert (NeoX, ratio 1, no floor, positions
 // present); its code carries none of the option checks below.
-template <int P, int W, int T, bool kLegacy, int kRope, bool kSanitize, bool kOptions>
+template <int P, int W, int T, int kFmt, int kRope, bool kSanitize, bool kOptions>
 __global__ __launch_bounds__(W * kWave) void insert_kernel(
     uint32_t n, uint32_t per_xcd, const u32x4 *kv, const int64_t *slots, const int64_t *positions,
     const f32x4 *cos_sin, uint32_t max_pos, uint32_t total_slots, uint8_t *base,
     int64_t page_stride, uint32_t block_size, uint32_t div_magic, uint32_t div_shift,
-    uint32_t ratio, uint32_t ratio_magic, uint32_t ratio_shift, uint32_t amax_floor_bits) {
+    uint32_t ratio, uint32_t ratio_magic, uint32_t ratio_shift, uint32_t amax_floor_bits,
+    const float *fp8_scale) {
   const InsertArgs a{kv,         slots,       positions, cos_sin,   base,    page_stride, n,
                      block_size, total_slots, div_magic, div_shift, max_pos};
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t t0 = (xcd_block(per_xcd) * W + wave) * T;
   if (t0 >= a.n) return;
+  // The per-tensor scale of the fp8 cache: one uniform load per wave.
+  float scale = 1.0f;
+  if constexpr (kFmt == kFmtFp8) scale = *fp8_scale;
 
+  // With a compression ratio above 1 most tokens are gated off, so the kv
+  // row is read only once the gate has passed; otherwise it is read at once,
+  // beside the slot and position.
+  const bool defer = kOptions && ratio > 1;
   u32x4 raw[T];
   uint32_t slot[T], row[T];
   bool ok[T];
@@ -379,8 +421,9 @@ __global__ __launch_bounds__(W * kWave) void insert_kernel(
   for (int k = 0; k < T; ++k) {
     const uint32_t t = t0 + k;
     const bool in = (T == 1) || t < a.n;
-    raw[k] = in ? ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t) * kWave + lane)
-                : u32x4{0, 0, 0, 0};
+    raw[k] = in && !defer
+                 ? ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t) * kWave + lane)
+                 : u32x4{0, 0, 0, 0};
     const int64_t sl = in ? a.slots[t] : -1;
     // No positions: only the rotation-free insert with ratio 1 (host-checked).
     const bool has_pos = !kOptions || positions != nullptr;
@@ -396,6 +439,8 @@ __global__ __launch_bounds__(W * kWave) void insert_kernel(
       const uint32_t q = (__umulhi(p1, ratio_magic) + p1) >> ratio_shift;
       ok[k] = ok[k] && p1 == q * ratio;
       row[k] = p1 - ratio;
+      if (ok[k])
+        raw[k] = ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t0 + k) * kWave + lane);
     }
   }
   // Only lanes 56..63 read (and later use) the cos/sin values. The empty asm
@@ -423,8 +468,8 @@ __global__ __launch_bounds__(W * kWave) void insert_kernel(
 #pragma unroll
   for (int k = 0; k < T; ++k)
     if (ok[k])
-      encode_store<P, kLegacy, kRope, kSanitize, kOptions>(a, lane, raw[k], c0[k], c1[k], s0[k],
-                                                           s1[k], slot[k], amax_floor_bits);
+      encode_store<P, kFmt, kRope, kSanitize, kOptions>(a, lane, raw[k], c0[k], c1[k], s0[k],
+                                                        s1[k], slot[k], amax_floor_bits, scale);
 }
 
 // bf16 of e4m3fn(code) * 2^(scale_byte - 127) for 8 codes, value k = byte k.
@@ -522,10 +567,10 @@ dim3 xcd_grid(int64_t waves, uint32_t *per_xcd) {
   return dim3(*per_xcd * kXcds);
 }
 
-template <int P, int W, int T, bool kLegacy, int kRope, bool kSanitize, bool kOptions>
+template <int P, int W, int T, int kFmt, int kRope, bool kSanitize, bool kOptions>
 hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
                          const int64_t *positions, const float *cos_sin, int64_t max_pos,
-                         const InsertOptions &o, hipStream_t stream) {
+                         const InsertOptions &o, const float *fp8_scale, hipStream_t stream) {
   uint32_t per_xcd = 0;
   const dim3 grid = xcd_grid<W>((n + T - 1) / T, &per_xcd);
   uint32_t n32 = static_cast<uint32_t>(n), mp = static_cast<uint32_t>(max_pos);
@@ -536,21 +581,23 @@ hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const in
   uint32_t total = g.total_slots, bs = g.block_size, magic = g.div_magic, shift = g.div_shift;
   uint32_t ratio = o.ratio, rmagic = o.ratio_magic, rshift = o.ratio_shift;
   uint32_t floor_bits = o.amax_floor_bits;
-  void *params[] = {&n32,  &per_xcd, &kv4,  &slots,  &positions, &cs4,   &mp,   &total,     &base,
-                    &stride, &bs,     &magic, &shift, &ratio,     &rmagic, &rshift, &floor_bits};
+  void *params[] = {&n32,  &per_xcd, &kv4,  &slots, &positions, &cs4,   &mp,
+                    &total, &base,    &stride, &bs,   &magic,     &shift, &ratio,
+                    &rmagic, &rshift, &floor_bits, &fp8_scale};
   return hipLaunchKernel(
-      reinterpret_cast<const void *>(insert_kernel<P, W, T, kLegacy, kRope, kSanitize, kOptions>),
+      reinterpret_cast<const void *>(insert_kernel<P, W, T, kFmt, kRope, kSanitize, kOptions>),
       grid,
       dim3(W * kWave), params, 0, stream);
 }
 
-template <bool kLegacy, int kRope, bool kSanitize, bool kOptions = true>
+template <int kFmt, int kRope, bool kSanitize, bool kOptions = true>
 hipError_t launch_insert_tuned(const void *kv, int64_t n, const CacheGeom &g,
                                const int64_t *slots, const int64_t *positions,
                                const float *cos_sin, int64_t max_pos, const InsertOptions &o,
-                               hipStream_t stream) {
-  return launch_insert<kInsertPolicy, kInsertWaves, kInsertTokens, kLegacy, kRope, kSanitize,
-                       kOptions>(kv, n, g, slots, positions, cos_sin, max_pos, o, stream);
+                               const float *fp8_scale, hipStream_t stream) {
+  return launch_insert<kInsertPolicy, kInsertWaves, kInsertTokens, kFmt, kRope, kSanitize,
+                       kOptions>(kv, n, g, slots, positions, cos_sin, max_pos, o, fp8_scale,
+                                 stream);
 }
 
 template <bool kLegacy, int R, int P, int W>
@@ -572,26 +619,33 @@ hipError_t launch_gather(const CacheGeom &g, const int32_t *indices, int64_t n, 
 
 hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
                          const int64_t *positions, const float *cos_sin, int64_t max_pos,
-                         bool legacy, const InsertOptions &o, hipStream_t stream) {
-  // The plain insert has its own instantiation; the options get one per
-  // (record, rotation, sanitise), with ratio and floor as uniform runtime
-  // values.
+                         Format format, const InsertOptions &o, const float *fp8_scale,
+                         hipStream_t stream) {
+  // The plain insert has its own instantiation per format; the options
+  // (packed formats only) get one per (record, rotation, sanitise), with
+  // ratio and floor as uniform runtime values.
   const bool plain = o.rope == kRopeNeox && !o.sanitize && o.ratio == 1 &&
                      o.amax_floor_bits == 0 && positions != nullptr;
-  if (plain)
-    return legacy ? launch_insert_tuned<true, kRopeNeox, false, false>(
-                        kv, n, g, slots, positions, cos_sin, max_pos, o, stream)
-                  : launch_insert_tuned<false, kRopeNeox, false, false>(
-                        kv, n, g, slots, positions, cos_sin, max_pos, o, stream);
-#define KVREC_INSERT(L, R, S)                                                               \
-  if (legacy == L && o.rope == R && o.sanitize == S)                                        \
-    return launch_insert_tuned<L, R, S>(kv, n, g, slots, positions, cos_sin, max_pos, o, \
+#define KVREC_PLAIN(F)                                                                        \
+  if (plain && format == static_cast<Format>(F))                                              \
+    return launch_insert_tuned<F, kRopeNeox, false, false>(kv, n, g, slots, positions, cos_sin, \
+                                                         max_pos, o, fp8_scale, stream);
+  KVREC_PLAIN(kFmtMxfp8)
+  KVREC_PLAIN(kFmtLegacy)
+  KVREC_PLAIN(kFmtBf16)
+  KVREC_PLAIN(kFmtFp8)
+#undef KVREC_PLAIN
+  if (format != Format::kMxfp8 && format != Format::kLegacy) return hipErrorInvalidValue;
+  const bool legacy = format == Format::kLegacy;
+#define KVREC_INSERT(L, R, S)                                                                   \
+  if (legacy == (L == kFmtLegacy) && o.rope == R && o.sanitize == S)                            \
+    return launch_insert_tuned<L, R, S>(kv, n, g, slots, positions, cos_sin, max_pos, o, nullptr, \
                                         stream);
 #define KVREC_INSERT_R(L, R) KVREC_INSERT(L, R, false) KVREC_INSERT(L, R, true)
 #define KVREC_INSERT_L(L) \
   KVREC_INSERT_R(L, kRopeNeox) KVREC_INSERT_R(L, kRopeInterleaved) KVREC_INSERT_R(L, kRopeNone)
-  KVREC_INSERT_L(false)
-  KVREC_INSERT_L(true)
+  KVREC_INSERT_L(kFmtMxfp8)
+  KVREC_INSERT_L(kFmtLegacy)
 #undef KVREC_INSERT_L
 #undef KVREC_INSERT_R
 #undef KVREC_INSERT

@@ -17,6 +17,11 @@ struct CacheGeom {
   uint32_t div_shift;    //   for every slot < 2^31
 };
 
+// Cache format written by the insert: the packed records (528 B MXFP8,
+// 584 B legacy) and the non-packed rows (1024 B bf16, 512 B e4m3fn with a
+// per-tensor scale).
+enum class Format : int { kMxfp8 = 0, kLegacy = 1, kBf16 = 2, kFp8 = 3 };
+
 // Validated insert options (see kvrec_insert_options in kvrec.h).
 struct InsertOptions {
   int rope;                  // 0 NeoX, 1 interleaved, 2 none
@@ -27,9 +32,12 @@ struct InsertOptions {
   uint32_t amax_floor_bits;  // fp32 bits of the amax floor (0 = none)
 };
 
+// fp8_scale (device, one fp32) is read only by Format::kFp8; the options
+// apply to the packed formats only (the non-packed ones take the defaults).
 hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
                          const int64_t *positions, const float *cos_sin, int64_t max_pos,
-                         bool legacy, const InsertOptions &o, hipStream_t stream);
+                         Format format, const InsertOptions &o, const float *fp8_scale,
+                         hipStream_t stream);
 hipError_t launch_gather_mxfp8(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
                                hipStream_t stream);
 hipError_t launch_gather_legacy(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,

@@ -262,6 +262,15 @@ def custom_insert(seed: int, n: int, record: int, block_size: int, num_blocks: i
         gather_indices=slots.astype(np.int32))
 
 
+def retarget(case: InsertCase, record: int, page_stride: Optional[int] = None) -> InsertCase:
+    """The same tokens, slots and positions written to another cache format
+    (e.g. the non-packed bf16 / fp8 caches), with that format's page stride
+    unless one is given."""
+    stride = page_stride if page_stride is not None else page_stride_for(record, case.block_size)
+    return dataclasses.replace(case, name=f"{case.name}_as_{record}", record=record,
+                               page_stride=stride)
+
+
 CONFIGS = {
     "mixed_1024": mixed_1024,
     "decode_16384": decode_16384,

@@ -45,6 +45,23 @@ def oracle_insert(case: W.InsertCase, backing: np.ndarray, kv_bits=None, slots=N
     return backing
 
 
+def oracle_insert_full(case: W.InsertCase, backing: np.ndarray, fp8_scale: float = 1.0,
+                       chunk: int = 8192) -> np.ndarray:
+    """The oracle's non-packed insert (record 1024 or 512), over token chunks."""
+    n = case.slot_mapping.shape[0]
+    jobs = [(a, min(n, a + chunk)) for a in range(0, n, chunk)]
+
+    def run(ab):
+        a, b = ab
+        oracle.insert_full(case.kv_bits[a:b], backing, case.num_blocks, case.page_stride,
+                           case.block_size, case.record, case.slot_mapping[a:b],
+                           case.positions[a:b], case.cos_sin, fp8_scale)
+
+    with cf.ThreadPoolExecutor(workers()) as ex:
+        list(ex.map(run, jobs))
+    return backing
+
+
 def oracle_gather(case_like, backing: np.ndarray, indices: np.ndarray,
                   chunk: int = 16384) -> np.ndarray:
     flat = np.ascontiguousarray(indices, np.int32).reshape(-1)
@@ -91,6 +108,14 @@ class DeviceCase:
                        self.slots if slots is None else slots,
                        self.positions if positions is None else positions,
                        self.cos_sin, self.case.block_size, **opts)
+
+    def insert_full(self, fp8_scale=None):
+        """Non-packed insert; ``fp8_scale`` a float (uploaded) or None."""
+        sc = None
+        if fp8_scale is not None:
+            sc = torch.tensor([fp8_scale], dtype=torch.float32, device=self.kv.device)
+        B.kvrec_insert_full(self.kv, self.k_cache, self.slots, self.positions, self.cos_sin,
+                            self.case.block_size, sc)
 
     def gather(self, indices: np.ndarray) -> np.ndarray:
         out = B.kvrec_gather(self.k_cache, dev(np.ascontiguousarray(indices, np.int32)))

@@ -75,7 +75,8 @@ def test_status_strings(lib):
 @pytest.mark.parametrize("record,bs,want", [
     (528, 32, 16896), (528, 64, 33792), (528, 128, 67584), (528, 256, 135168),
     (584, 32, 19008), (584, 64, 37440), (584, 128, 74880), (584, 256, 149760),
-    (528, 1, 1024), (528, 4, 2560), (584, 4, 2880), (584, 1, 1152)])
+    (528, 1, 1024), (528, 4, 2560), (584, 4, 2880), (584, 1, 1152),
+    (1024, 1, 1024), (1024, 64, 65536), (512, 3, 1536), (512, 64, 32768)])
 def test_page_stride(lib, record, bs, want):
     out = ctypes.c_int64(-1)
     assert lib.kvrec_page_stride(record, bs, ctypes.byref(out)) == OK
@@ -85,9 +86,14 @@ def test_page_stride(lib, record, bs, want):
 def test_page_stride_errors(lib):
     out = ctypes.c_int64(-1)
     assert lib.kvrec_page_stride(528, 64, None) == NULL
-    assert lib.kvrec_page_stride(512, 64, ctypes.byref(out)) == RECORD
+    assert lib.kvrec_page_stride(513, 64, ctypes.byref(out)) == RECORD
     assert lib.kvrec_page_stride(576, 64, ctypes.byref(out)) == RECORD
     assert lib.kvrec_page_stride(528, 0, ctypes.byref(out)) == BLOCK
+    # a page of 2^31 bytes or more would overflow the kernels' 32-bit offsets
+    assert lib.kvrec_page_stride(1024, 2 ** 21, ctypes.byref(out)) == OK
+    assert lib.kvrec_page_stride(1024, 2 ** 21 + 1, ctypes.byref(out)) == BLOCK
+    assert lib.kvrec_page_stride(528, 2 ** 22, ctypes.byref(out)) == BLOCK
+    out.value = -1
     assert out.value == -1
 
 
@@ -181,6 +187,53 @@ def test_insert_options_validation(lib):
     assert lib.kvrec_status_str(OPTION) == b"insert option out of range"
 
 
+def test_page_size_limit(lib):
+    # block_size * record above 2^31 is refused before anything else about the page
+    big = 2 ** 22 * 528
+    assert ins(lib, cache(nb=1, bs=2 ** 22, stride=big), bs=2 ** 22) == BLOCK
+    assert gat(lib, cache(nb=1, bs=2 ** 22, stride=big)) == BLOCK
+    ok_bs = 2 ** 31 // 528 // 512 * 512  # largest multiple of 512 slots under the limit
+    assert ins(lib, cache(nb=1, bs=ok_bs, stride=ok_bs * 528), n=0, bs=ok_bs) == OK
+
+
+def full(lib, c, n=8, kv=FAKE, slots=FAKE, pos=FAKE, cs=FAKE, max_pos=16, bs=64, rec=1024,
+         scale=None):
+    return lib.kvrec_insert_full(kv, n, ctypes.byref(c) if c is not None else None, slots, pos,
+                                 cs, max_pos, bs, rec, scale, None)
+
+
+def test_insert_full_validation(lib):
+    bf = cache(rec=1024, stride=65536)
+    f8 = cache(rec=512, stride=32768)
+    assert full(lib, bf, n=0) == OK
+    assert full(lib, f8, n=0, rec=512, scale=FAKE) == OK
+    assert full(lib, bf, n=0, kv=None, slots=None, pos=None, cs=None) == OK
+    assert full(lib, None) == NULL
+    assert full(lib, cache(base=None, rec=1024, stride=65536)) == NULL
+    assert full(lib, f8, rec=512) == NULL                        # the fp8 cache needs its scale
+    assert full(lib, f8, rec=512, n=0) == NULL
+    assert full(lib, bf, scale=FAKE) == OPTION                   # a bf16 cache takes none
+    for arg in ("kv", "slots", "pos", "cs"):
+        assert full(lib, bf, **{arg: None}) == NULL, arg
+    assert full(lib, bf, rec=512) == RECORD                      # != cache record
+    assert full(lib, cache(), rec=528) == RECORD                 # packed: not this call
+    assert full(lib, cache(rec=584, stride=37440), rec=584) == RECORD
+    assert full(lib, bf, bs=32) == BLOCK
+    assert full(lib, cache(rec=1024, stride=65536 - 16)) == STRIDE
+    assert full(lib, cache(rec=1024, stride=65536 + 8)) == STRIDE  # not a multiple of 16
+    assert full(lib, cache(rec=1024, stride=65536 + 16), n=0) == OK
+    assert full(lib, cache(rec=512, stride=32768 + 48), rec=512, scale=FAKE, n=0) == OK
+    assert full(lib, bf, n=-1) == SIZE
+    assert full(lib, bf, max_pos=0) == SIZE
+    assert full(lib, bf, kv=FAKE + 8) == ALIGN
+    assert full(lib, f8, rec=512, scale=FAKE + 2) == ALIGN
+    # the packed calls refuse the non-packed records
+    assert ins(lib, bf, rec=1024) == RECORD
+    assert ins_ex(lib, f8, None, rec=512) == RECORD
+    assert gat(lib, bf) == RECORD
+    assert gat(lib, f8) == RECORD
+
+
 def test_legacy_cache_accepted(lib):
     assert ins(lib, cache(rec=584, stride=37440), n=0, rec=584) == OK
     assert gat(lib, cache(rec=584, stride=37440), n=0) == OK
@@ -196,14 +249,38 @@ def test_python_binding_rejects_cpu_tensors():
                        torch.zeros(4, dtype=torch.int64), torch.zeros(8, 64), 4)
     with pytest.raises(ValueError):
         B.kvrec_gather(torch.zeros(1, 4, 528, dtype=torch.uint8), torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        B.kvrec_insert_full(kv, torch.zeros(1, 4, 512, dtype=torch.bfloat16),
+                            torch.zeros(4, dtype=torch.int64), torch.zeros(4, dtype=torch.int64),
+                            torch.zeros(8, 64), 4)
+
+
+def _kernel_bodies(asm: str) -> dict:
+    bodies = {}
+    for name in re.findall(r"^(_Z\S+):", asm, re.M):
+        b = asm[asm.index(name + ":"):]
+        b = b[:b.index(".Lfunc_end")]
+        bodies[name] = [l.split()[0] for l in (x.strip() for x in b.splitlines())
+                        if l and not l.startswith((";", ".", "_"))]
+    return bodies
 
 
 def test_kernels_have_no_fma_and_no_packed_fp32():
+    """No contraction: the rotation's products and sums are rounded one by
+    one. The only fused multiply-adds allowed are the five inside each IEEE
+    fp32 division sequence (ending in v_div_fixup_f32) of the fp8 cache."""
     asm = KB.device_asm()
     code = "\n".join(l for l in asm.splitlines() if not l.lstrip().startswith((";", ".")))
-    for op in ("v_fma_f32", "v_fmac_f32", "v_mad_f32", "v_mac_f32", "v_fma_mix",
+    for op in ("v_mad_f32", "v_mac_f32", "v_fma_mix",
                "v_pk_fma_f32", "v_pk_mul_f32", "v_pk_add_f32"):
         assert op not in code, op
+    divs = 0
+    for name, ops in _kernel_bodies(asm).items():
+        fma = sum(op.startswith(("v_fma_f32", "v_fmac_f32")) for op in ops)
+        fixup = sum(op.startswith("v_div_fixup_f32") for op in ops)
+        assert fma == 5 * fixup, (name, fma, fixup)
+        divs += fixup
+    assert divs > 0  # the fp8 cache's kernel divides
     # fp32 denormals preserved for every kernel (mode 3 = keep inputs and outputs)
     modes = re.findall(r"\.amdhsa_float_denorm_mode_32\s+(\d+)", asm)
     assert modes and set(modes) == {"3"}

@@ -1,0 +1,130 @@
+"""GPU parity of the non-packed cache insert (kvrec_insert_full): bf16 rows
+and e4m3fn rows with one fp32 per-tensor scale, the KV-only op's other two
+cache formats ([KV-only op] 实现拆解 1). Every byte of the pre-filled cache
+backing is compared with the oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from quantized_paged_kv_rope_amd import binding as B
+from quantized_paged_kv_rope_amd import workloads as W
+from tests import parity_util as P
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [W.RECORD_BF16, W.RECORD_FP8]
+FP8_SCALES = [1.0, 0.0123, 3.7, 1e-38, 3e38]  # 1e-38 saturates, 3e38 underflows
+
+
+def _scales(record):
+    return [None] if record == W.RECORD_BF16 else FP8_SCALES
+
+
+def _oracle(case, scale):
+    return P.oracle_insert_full(case, case.initial_backing(), 1.0 if scale is None else scale)
+
+
+@pytest.mark.parametrize("record", FORMATS)
+def test_full_worked_token(golden, record):
+    fc = golden["full_cache"]
+    inp = fc["inputs"]
+    x = np.zeros((2, 512), np.float32)
+    for d, v in inp["kv_nonzero_token0"]:
+        x[0, d] = float(v)
+    x[1, :] = 1.0
+    table = np.zeros((inp["max_pos"], 64), np.float32)
+    table[:, :32] = 1.0
+    table[3, 0], table[3, 32] = 0.5, 0.75
+    exp = fc["bf16_cache" if record == W.RECORD_BF16 else "fp8_cache"]
+    case = W.InsertCase("full_worked", record, inp["block_size"], inp["num_blocks"],
+                        exp["page_stride"], W.to_bf16_bits(x),
+                        np.array([t["slot"] for t in inp["tokens"]], np.int64),
+                        np.array([t["position"] for t in inp["tokens"]], np.int64), table,
+                        backing_seed=33)
+    scale = None if record == W.RECORD_BF16 else inp["fp8_scale"]
+    d = P.DeviceCase(case)
+    d.insert_full(scale)
+    got = d.backing_host()
+    at = exp["row_offset"]
+    if record == W.RECORD_BF16:
+        want_row = np.zeros(512, np.uint16)
+        for dim, v in exp["elements_nonzero"]:
+            want_row[dim] = v
+        assert got[at: at + 1024].view(np.uint16).tolist() == want_row.tolist()
+    else:
+        want_row = np.zeros(512, np.uint8)
+        for dim, v in exp["codes_nonzero"]:
+            want_row[dim] = v
+        assert got[at: at + 512].tolist() == want_row.tolist()
+    want = _oracle(case, scale)
+    assert np.array_equal(got, want), P.first_diff(got, want)
+
+
+@pytest.mark.parametrize("record", FORMATS)
+@pytest.mark.parametrize("n,bs,pad", [(1, 64, 0), (17, 16, 16), (1023, 64, 48), (4099, 3, 0)])
+def test_full_whole_backing(record, n, bs, pad):
+    nb = (n * 5 // 4) // bs + 2
+    stride = W.page_stride_for(record, bs) + pad
+    case = W.custom_insert(4000 + n + bs + record, n, record, bs, nb, max_pos=700,
+                           page_stride=stride, scale_rows=True)
+    d = P.DeviceCase(case)
+    kv_before = P.host_bits(d.kv).copy()
+    for scale in _scales(record):
+        d.backing.copy_(P.dev(case.initial_backing()))
+        d.insert_full(scale)
+        got = d.backing_host()
+        want = _oracle(case, scale)
+        assert np.array_equal(got, want), (scale, P.first_diff(got, want))
+    assert np.array_equal(P.host_bits(d.kv), kv_before), "kv was modified"
+
+
+@pytest.mark.parametrize("record", FORMATS)
+def test_typed_cache_views(record):
+    """The page's op takes these caches as bf16 / float8_e4m3fn tensors
+    [num_blocks, block_size, 512]; such a view (padded page stride included)
+    writes the same bytes as the uint8 view."""
+    bs, pad = 16, 32
+    stride = W.page_stride_for(record, bs) + pad
+    case = W.custom_insert(555 + record, 300, record, bs, 25, max_pos=400, page_stride=stride)
+    scale = None if record == W.RECORD_BF16 else 0.37
+    d = P.DeviceCase(case)
+    dtype = torch.bfloat16 if record == W.RECORD_BF16 else torch.float8_e4m3fn
+    item = 2 if record == W.RECORD_BF16 else 1
+    typed = d.backing.view(dtype).as_strided((case.num_blocks, bs, 512), (stride // item, 512, 1))
+    sc = None if scale is None else torch.tensor([scale], dtype=torch.float32, device="cuda")
+    B.kvrec_insert_full(d.kv, typed, d.slots, d.positions, d.cos_sin, bs, sc)
+    got = d.backing_host()
+    want = _oracle(case, scale)
+    assert np.array_equal(got, want), P.first_diff(got, want)
+
+
+@pytest.mark.parametrize("record", FORMATS)
+def test_full_all_skipped_and_empty(record):
+    case = W.custom_insert(808 + record, 64, record, 8, 10, max_pos=100)
+    case.slot_mapping[:] = -1
+    scale = None if record == W.RECORD_BF16 else 2.0
+    d = P.DeviceCase(case)
+    d.insert_full(scale)
+    assert np.array_equal(d.backing_host(), case.initial_backing())
+    sc = None if scale is None else torch.tensor([scale], dtype=torch.float32, device="cuda")
+    B.kvrec_insert_full(d.kv[:0], d.k_cache, d.slots[:0], d.positions[:0], d.cos_sin, 8, sc)
+    assert np.array_equal(d.backing_host(), case.initial_backing())
+
+
+@pytest.mark.parametrize("record", FORMATS)
+def test_full_prefill_262144(record):
+    """The prefill workload's tokens (262144 at positions 0..) into a 4096-page
+    non-packed cache, in the launch configuration the benchmark times; every
+    byte compared."""
+    case = W.retarget(W.prefill_262144(), record)
+    scale = None if record == W.RECORD_BF16 else 0.0625
+    d = P.DeviceCase(case)
+    d.insert_full(scale)
+    got = d.backing_host()
+    want = _oracle(case, scale)
+    assert np.array_equal(got, want), P.first_diff(got, want)
+    del d
+    torch.cuda.empty_cache()
