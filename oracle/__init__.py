@@ -95,6 +95,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_rope_rows_ex.restype = None
     L.orc_insert_full.argtypes = [p, i64, p, i64, i64, i32, i32, p, p, p, i64, ctypes.c_float]
     L.orc_insert_full.restype = ctypes.c_int
+    L.orc_qnorm_rope.argtypes = [p, i64, i32, p, p, i64, ctypes.c_double, i32, p]
+    L.orc_qnorm_rope.restype = None
     L.orc_gather.argtypes = [p, i64, i64, i32, i32, p, i64, p]
     L.orc_gather.restype = ctypes.c_int
     L.orc_e4m3_encode_f32.argtypes = [p, i64, p]
@@ -278,6 +280,27 @@ def insert_full(kv_bits: np.ndarray, backing: np.ndarray, num_blocks: int, page_
                                _ptr(cos_sin), cos_sin.shape[0], float(fp8_scale))
     if rc != 0:
         raise ValueError(f"oracle full-cache insert rejected record={record}")
+
+
+def qnorm_rope(q_bits: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray, eps: float,
+               apply_norm: bool = True, out: np.ndarray = None) -> np.ndarray:
+    """q side of the attention write: bf16 bits [n, heads, 512] -> bf16 bits.
+    Rows of tokens whose position is out of range keep ``out``'s contents
+    (a copy of the input when ``out`` is None)."""
+    q_bits = _c(q_bits, np.uint16)
+    positions = _c(positions, np.int64)
+    cos_sin = _c(cos_sin, np.float32)
+    if q_bits.ndim != 3 or q_bits.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [n, heads, 512]")
+    n, heads = q_bits.shape[:2]
+    if positions.shape[0] < n or cos_sin.ndim != 2 or cos_sin.shape[1] != 64:
+        raise ValueError("positions must cover every token; cos_sin is [max_pos, 64]")
+    if out is None:
+        out = q_bits.copy()
+    out = _c(out, np.uint16)
+    lib().orc_qnorm_rope(_ptr(q_bits), n, heads, _ptr(positions), _ptr(cos_sin),
+                         cos_sin.shape[0], float(eps), int(bool(apply_norm)), _ptr(out))
+    return out
 
 
 def gather(backing: np.ndarray, num_blocks: int, page_stride: int, block_size: int,

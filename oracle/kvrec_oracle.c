@@ -361,6 +361,59 @@ int orc_insert_full(const uint16_t *kv, int64_t n, uint8_t *cache, int64_t num_b
 }
 
 /* ------------------------------------------------------------------------ */
+/* q side of the attention write (the QNorm op whose q_in, q_head_padded,    */
+/* eps and apply_q_norm arguments [KV-only op, 实现拆解 1] lists, called in   */
+/* [MXFP8 record, 关键源码片段] with padded_heads and eps). The pages name   */
+/* the arguments only; the readings taken:                                   */
+/*   - q is bf16 [n, heads, 512]; every head of every token is processed      */
+/*     (the slot only decides the cache write);                              */
+/*   - the norm is an RMSNorm over the head's 512 dims with no weight (none  */
+/*     is passed): y = x / sqrt(mean(x^2) + eps); without the norm y = x;    */
+/*   - then the same NeoX rotation of dims 448..511 as the KV insert, with   */
+/*     the token's table row;                                                */
+/*   - each output element is the bf16 nearest to the exact result. It is    */
+/*     computed here in binary64 (the sum of squares, the root, the products */
+/*     and the rotation), rounded to bf16 once.                             */
+/* A token whose position is outside [0, max_pos) leaves its q_out rows      */
+/* unwritten.                                                                */
+/* ------------------------------------------------------------------------ */
+void orc_qnorm_rope(const uint16_t *q_in, int64_t n, int32_t heads, const int64_t *positions,
+                    const float *cos_sin_cache, int64_t max_pos, double eps, int32_t apply_norm,
+                    uint16_t *q_out) {
+  int64_t t;
+  int32_t h;
+  int d, i;
+  for (t = 0; t < n; ++t) {
+    int64_t pos = positions[t];
+    const float *cs;
+    if (pos < 0 || pos >= max_pos) continue;
+    cs = cos_sin_cache + pos * ROPE_DIM;
+    for (h = 0; h < heads; ++h) {
+      const uint16_t *x = q_in + (t * heads + h) * HEAD_DIM;
+      uint16_t *out = q_out + (t * heads + h) * HEAD_DIM;
+      double y[HEAD_DIM];
+      double scale = 1.0;
+      if (apply_norm) {
+        double sum = 0.0;
+        for (d = 0; d < HEAD_DIM; ++d) {
+          double v = (double)widen_bf16(x[d]);
+          sum += v * v;
+        }
+        scale = 1.0 / sqrt(sum / HEAD_DIM + eps);
+      }
+      for (d = 0; d < HEAD_DIM; ++d) y[d] = (double)widen_bf16(x[d]) * scale;
+      for (i = 0; i < HALF_ROPE; ++i) {
+        double c = cs[i], s = cs[HALF_ROPE + i];
+        double y1 = y[NOPE_DIM + i], y2 = y[NOPE_DIM + HALF_ROPE + i];
+        y[NOPE_DIM + i] = y1 * c - y2 * s;
+        y[NOPE_DIM + HALF_ROPE + i] = y2 * c + y1 * s;
+      }
+      for (d = 0; d < HEAD_DIM; ++d) out[d] = orc_bf16_round(y[d]);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Gather (dequantise to bf16). Index = page * block_size + offset; a       */
 /* negative index marks an invalid entry [FlashMLA, sparse decode           */
 /* integration notes] and yields a row of +0. Reading: an index >=          */

@@ -87,6 +87,15 @@ int orc_insert_full(const uint16_t *kv, int64_t n, uint8_t *cache, int64_t num_b
                     const int64_t *slot_mapping, const int64_t *positions,
                     const float *cos_sin_cache, int64_t max_pos, float fp8_scale);
 
+/* q side of the attention write: per token and head (q bf16 [n, heads, 512]),
+ * y = x / sqrt(mean(x^2) + eps) if apply_norm (else y = x), the NeoX
+ * rotation of dims 448..511 with the token's table row, and the bf16 nearest
+ * to each exact result (binary64 arithmetic, one rounding). Tokens with a
+ * position outside [0, max_pos) leave q_out unwritten. q_out may be q_in. */
+void orc_qnorm_rope(const uint16_t *q_in, int64_t n, int32_t heads, const int64_t *positions,
+                    const float *cos_sin_cache, int64_t max_pos, double eps, int32_t apply_norm,
+                    uint16_t *q_out);
+
 /* Gather n records back to bf16 rows.
  *   token_indices [n] int32, page * block_size + offset; negative -> zeros
  *   out           bf16 bits [n, 512]
