@@ -97,6 +97,9 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_insert_full.restype = ctypes.c_int
     L.orc_qnorm_rope.argtypes = [p, i64, i32, p, p, i64, ctypes.c_double, i32, p]
     L.orc_qnorm_rope.restype = None
+    L.orc_expand_candidates.argtypes = [p, i64, p, i64, p, i64, i64, i32, i32, i32, p, i64, p,
+                                        i64]
+    L.orc_expand_candidates.restype = ctypes.c_int
     L.orc_gather.argtypes = [p, i64, i64, i32, i32, p, i64, p]
     L.orc_gather.restype = ctypes.c_int
     L.orc_e4m3_encode_f32.argtypes = [p, i64, p]
@@ -301,6 +304,26 @@ def qnorm_rope(q_bits: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray, e
     lib().orc_qnorm_rope(_ptr(q_bits), n, heads, _ptr(positions), _ptr(cos_sin),
                          cos_sin.shape[0], float(eps), int(bool(apply_norm)), _ptr(out))
     return out
+
+
+def expand_candidates(cand: np.ndarray, row_ks: np.ndarray, row_ke: np.ndarray, ratio: int,
+                      sparse_block: int):
+    """Candidate-block expansion: int32 cand [rows, K], ks/ke [rows] ->
+    (sparse_indices int32 [rows, K * ratio], end int32 [rows])."""
+    cand = _c(cand, np.int32)
+    row_ks = _c(row_ks, np.int32)
+    row_ke = _c(row_ke, np.int32)
+    rows, k = cand.shape
+    if row_ks.shape[0] < rows or row_ke.shape[0] < rows:
+        raise ValueError("ks and ke must cover every row")
+    sparse = np.empty((rows, k * ratio), np.int32)
+    end = np.empty(rows, np.int32)
+    rc = lib().orc_expand_candidates(_ptr(cand), k, _ptr(row_ks), 1, _ptr(row_ke), 1, rows, k,
+                                     int(ratio), int(sparse_block), _ptr(sparse), k * ratio,
+                                     _ptr(end), 1)
+    if rc != 0:
+        raise ValueError(f"oracle expansion rejected K={k} ratio={ratio} SBK={sparse_block}")
+    return sparse, end
 
 
 def gather(backing: np.ndarray, num_blocks: int, page_stride: int, block_size: int,

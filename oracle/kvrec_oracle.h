@@ -12,6 +12,8 @@
  *   [KV-only op]    vLLM PR #56441 report, "[Perf][DSpark] Add KV-only context
  *                   insertion across V4.1 cache formats"
  *   [FlashMLA]      article page "deepseek-ai/FlashMLA" (ssnai.com)
+ *   [Sparse indexer] vLLM PR #56254 report, "[DSA] Wire DeepGEMM sparse MQA
+ *                   logits into the DeepSeek V4.1 indexer"
  * Where the pages leave a step open, the reading taken is stated at the
  * function. All integers are host-endian (little-endian x86-64).
  */
@@ -103,6 +105,23 @@ void orc_qnorm_rope(const uint16_t *q_in, int64_t n, int32_t heads, const int64_
 int orc_gather(const uint8_t *cache, int64_t num_blocks, int64_t page_stride,
                int32_t block_size, int32_t record,
                const int32_t *token_indices, int64_t n, uint16_t *out);
+
+/* Candidate-block expansion of the sparse indexer ([Sparse indexer]
+ * 关键源码片段, _expand_candidates_kernel), for `rows` rows:
+ *   cand        int32 [rows, K] (row stride cand_stride elements)
+ *   row_ks/ke   int32 per row (strides ks_stride / ke_stride): the row's KV
+ *               range [ks, ke)
+ *   ratio       1 or 2 (2 splits a candidate c into sparse blocks 2c, 2c+1)
+ *   sparse_block SBK, tokens per sparse block
+ *   sparse      int32 [rows, K * ratio] out: the sorted kept blocks + ks/SBK,
+ *               padded with the last one
+ *   end         int32 per row out: valid sparse token columns
+ * Returns 0, or -1 for a bad K / ratio / SBK (or no memory). */
+int orc_expand_candidates(const int32_t *cand, int64_t cand_stride, const int32_t *row_ks,
+                          int64_t ks_stride, const int32_t *row_ke, int64_t ke_stride,
+                          int64_t rows, int32_t num_candidates, int32_t ratio,
+                          int32_t sparse_block, int32_t *sparse, int64_t sparse_stride,
+                          int32_t *end, int64_t end_stride);
 
 /* ---- batch forms of the element codecs, for the pin tests -------------- */
 
