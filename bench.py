@@ -188,6 +188,33 @@ def all_configs_report(dev, out=sys.stderr) -> list:
             lambda: B.kvrec_gather(kc, idx, out=o))
         del backing, kc, kv, o
         torch.cuda.empty_cache()
+    # the attention write: q RMSNorm + RoPE over 128 heads fused with the insert
+    aw = W.attention_write()
+    ac = aw.insert
+    q = up(aw.q_bits.view(np.int16)).view(torch.bfloat16)
+    qo = torch.empty_like(q)
+    kv = up(ac.kv_bits.view(np.int16)).view(torch.bfloat16)
+    sl, ps, cs = up(ac.slot_mapping), up(ac.positions), up(ac.cos_sin)
+    backing, kc = B.alloc_cache(ac.num_blocks, ac.block_size, ac.record, ac.page_stride,
+                                device=dev)
+    heads = aw.q_bits.shape[1]
+    ab = ac.num_tokens * (1824 + 2048 * heads)
+    add(aw.name, f"qkv {heads}h 528", ac.num_tokens, ac.num_tokens, ab,
+        lambda: B.kvrec_qnorm_rope_insert(q, kv, kc, sl, ps, cs, ac.block_size, eps=aw.eps,
+                                          q_out=qo))
+    del q, qo, kv, backing, kc
+    torch.cuda.empty_cache()
+    # the sparse indexer's candidate-block expansion (integer; per row: the
+    # candidates, ks and ke in, the sparse indices and end out)
+    sx = W.sparse_expand()
+    xc, xks, xke = up(sx.cand), up(sx.row_ks), up(sx.row_ke)
+    xrows, k = sx.cand.shape
+    xout = (torch.empty((xrows, k * sx.ratio), dtype=torch.int32, device=dev),
+            torch.empty(xrows, dtype=torch.int32, device=dev))
+    xb = xrows * (4 * k + 8 + 4 * k * sx.ratio + 4)
+    add(sx.name, f"expand r{sx.ratio} sbk{sx.sparse_block}", xrows, xrows, xb,
+        lambda: B.kvrec_expand_candidates(xc, xks, xke, sx.ratio, sx.sparse_block, out=xout))
+    del xc, xks, xke, xout
     tk = W.topk_gather()
     backing, kc = B.alloc_cache(tk.num_blocks, tk.block_size, tk.record, tk.page_stride, device=dev)
     cs = up(tk.cos_sin())

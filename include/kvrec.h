@@ -8,7 +8,12 @@
  *                 quantisation + paged store of the token's record
  *                 (kvrec_insert_ex adds the compressed-KV options;
  *                 kvrec_insert_full writes the non-packed bf16 / fp8 caches);
- *   kvrec_gather  the inverse: paged read + dequantisation to bf16 rows.
+ *   kvrec_gather  the inverse: paged read + dequantisation to bf16 rows;
+ *   kvrec_qnorm_rope_insert  the attention write: q RMSNorm + RoPE for every
+ *                 head, fused with kvrec_insert in one launch;
+ *   kvrec_expand_candidates  the sparse indexer's candidate-block expansion
+ *                 into the sorted sparse block indices that select what the
+ *                 attention reads.
  *
  * Sources (page titles; sections named as on the pages):
  *   [MXFP8 record] vLLM PR #56893 report, "[Model][DSv4.1] Store the whole KV
@@ -16,6 +21,8 @@
  *   [KV-only op]   vLLM PR #56441 report, "[Perf][DSpark] Add KV-only context
  *                  insertion across V4.1 cache formats"
  *   [FlashMLA]     article page "deepseek-ai/FlashMLA" (ssnai.com)
+ *   [Sparse indexer] vLLM PR #56254 report, "[DSA] Wire DeepGEMM sparse MQA
+ *                  logits into the DeepSeek V4.1 indexer"
  *
  * Conventions for every call:
  *   - Pointers marked (device) are HIP device memory of the current device;
@@ -84,7 +91,8 @@ typedef enum kvrec_status {
   KVREC_ERR_SIZE = -6,        /* negative count, max_pos < 1, or a size
                                  beyond what the kernels index            */
   KVREC_ERR_HIP = -7,         /* the HIP launch reported an error         */
-  KVREC_ERR_OPTION = -8       /* an insert option is out of range         */
+  KVREC_ERR_OPTION = -8,      /* an insert option is out of range         */
+  KVREC_ERR_OVERLAP = -9      /* an output partly overlaps an input       */
 } kvrec_status;
 
 /* A paged cache: num_blocks pages, page_stride bytes apart, each holding
@@ -205,6 +213,72 @@ int kvrec_insert_full(const void *kv, int64_t num_tokens, const kvrec_cache *k_c
                       const int64_t *slot_mapping, const int64_t *positions,
                       const float *cos_sin_cache, int64_t max_pos, int32_t block_size,
                       int32_t record, const float *fp8_scale, kvrec_stream stream);
+
+/* The attention write: the q side of the QNorm op ([KV-only op] 实现拆解 1
+ * lists its q_in, q_head_padded, eps and apply_q_norm arguments; [MXFP8
+ * record] 关键源码片段 calls it with padded_heads and eps) fused with
+ * kvrec_insert, in one launch. The pages name these arguments only; the
+ * readings: every head of every token is processed (the slot only decides
+ * the cache write), the norm is an RMSNorm over the head's 512 dims with no
+ * weight, and q is rotated like the KV latent (NeoX pairs of dims 448..511,
+ * the token's table row).
+ *
+ *   q_in          (device) bf16 [num_tokens, num_heads, 512], contiguous,
+ *                 16-B aligned.
+ *   q_out         (device) same shape; q_in itself (in place) or a buffer
+ *                 that does not overlap it (KVREC_ERR_OVERLAP otherwise).
+ *   num_heads     1 .. 1024 (the padded head count); num_tokens * num_heads
+ *                 <= 2^30.
+ *   eps           with apply_q_norm: finite and > 0 (KVREC_ERR_OPTION).
+ *   apply_q_norm  0: rotation only; 1: y = x / sqrt(mean(x^2) + eps) first.
+ *   the rest      as kvrec_insert (packed records 528 / 584 only).
+ *
+ * Per head, in fp32: the sum of squares (products and sums rounded one by
+ * one, in a fixed order), inv = an approximation of 1 / sqrt(sum / 512 +
+ * eps) within 1 ulp, y = x * inv, the rotation as in kvrec_insert, and bf16
+ * nearest even. The sum order is not the oracle's, so q_out agrees with the
+ * exact result to within the error bound of this arithmetic, not bit for
+ * bit; the cache bytes are exactly those of kvrec_insert. A token whose
+ * position is outside [0, max_pos) leaves its q_out rows unwritten. */
+int kvrec_qnorm_rope_insert(const void *q_in, void *q_out, int32_t num_heads, float eps,
+                            int32_t apply_q_norm, const void *kv, int64_t num_tokens,
+                            const kvrec_cache *k_cache, const int64_t *slot_mapping,
+                            const int64_t *positions, const float *cos_sin_cache,
+                            int64_t max_pos, int32_t block_size, int32_t record,
+                            kvrec_stream stream);
+
+/* Candidate-block expansion ([Sparse indexer] 关键源码片段: the per-row
+ * program _expand_candidates_kernel and candidate_blocks_to_sparse_indices).
+ * For each of `rows` rows, in the page's order:
+ *   - take the row's K candidate block ids; with ratio 2 each candidate c
+ *     becomes the two sparse blocks 2c and 2c + 1 (a candidate block of
+ *     2 * SBK tokens split in two);
+ *   - keep the blocks b with 0 <= b < ceil(max(ke - ks, 0) / SBK);
+ *   - sort them ascending (duplicates kept) and add base = ks / SBK;
+ *   - write them to the row's K * ratio outputs, padding after the n_valid
+ *     kept ones with the last kept block + base (base when none is kept);
+ *   - end = (n_valid - 1) * SBK + min(max(ke - (last * SBK + ks), 1), SBK),
+ *     or 0 when nothing is kept (only the last block can be partial).
+ * Integer arithmetic is exact (no int32 wrap of intermediate values).
+ *
+ *   candidate_blocks (device) int32, row r at r * cand_stride (elements),
+ *                    K entries; cand_stride >= K.
+ *   row_ks, row_ke   (device) int32, row r at r * ks_stride / r * ke_stride
+ *                    (>= 1): the row's KV range [ks, ke). The caller keeps
+ *                    ks >= 0 and ke >= 0.
+ *   rows             0 .. 2^30; 0 returns KVREC_OK without a launch.
+ *   num_candidates   K, a power of two, K * ratio <= 1024 (KVREC_ERR_SIZE).
+ *   ratio            1 or 2; sparse_block (SBK) 8 or 16 (KVREC_ERR_OPTION).
+ *   sparse_indices   (device) int32 out, row r at r * sparse_stride, K * ratio
+ *                    entries; sparse_stride >= K * ratio.
+ *   end              (device) int32 out, row r at r * end_stride (>= 1).
+ * All pointers 4-B aligned; outputs must not overlap the inputs. */
+int kvrec_expand_candidates(const int32_t *candidate_blocks, int64_t cand_stride,
+                            const int32_t *row_ks, int64_t ks_stride, const int32_t *row_ke,
+                            int64_t ke_stride, int64_t rows, int32_t num_candidates,
+                            int32_t ratio, int32_t sparse_block, int32_t *sparse_indices,
+                            int64_t sparse_stride, int32_t *end, int64_t end_stride,
+                            kvrec_stream stream);
 
 /* Gather num_indices records back to bf16 rows ([MXFP8 record] 实现拆解 4:
  * one gather parameterised by the record; [FlashMLA]: index =

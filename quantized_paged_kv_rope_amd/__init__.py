@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     KvrecError,
     alloc_cache,
     cache_descriptor,
+    kvrec_expand_candidates,
     kvrec_gather,
     insert_options,
     kvrec_insert,
@@ -25,6 +26,7 @@ from .binding import (  # noqa: F401
     kvrec_insert_full,
     kvrec_insert_options,
     kvrec_page_stride,
+    kvrec_qnorm_rope_insert,
     kvrec_status_str,
     load_library,
 )

@@ -45,10 +45,11 @@ KVREC_OK = 0
 STATUS_NAMES = {
     0: "KVREC_OK", -1: "KVREC_ERR_NULL", -2: "KVREC_ERR_RECORD", -3: "KVREC_ERR_BLOCK_SIZE",
     -4: "KVREC_ERR_PAGE_STRIDE", -5: "KVREC_ERR_ALIGNMENT", -6: "KVREC_ERR_SIZE",
-    -7: "KVREC_ERR_HIP", -8: "KVREC_ERR_OPTION",
+    -7: "KVREC_ERR_HIP", -8: "KVREC_ERR_OPTION", -9: "KVREC_ERR_OVERLAP",
 }
 EXPORTED_SYMBOLS = ("kvrec_page_stride", "kvrec_insert", "kvrec_insert_ex", "kvrec_insert_full",
-                    "kvrec_gather", "kvrec_status_str")
+                    "kvrec_qnorm_rope_insert", "kvrec_expand_candidates", "kvrec_gather",
+                    "kvrec_status_str")
 ROPE = {"neox": 0, "interleaved": 1, "none": 2}
 
 
@@ -115,6 +116,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvrec_insert_full.argtypes = [p, i64, ctypes.POINTER(kvrec_cache), p, p, p, i64, i32, i32,
                                     p, p]
     L.kvrec_insert_full.restype = ctypes.c_int
+    L.kvrec_qnorm_rope_insert.argtypes = [p, p, i32, ctypes.c_float, i32, p, i64,
+                                          ctypes.POINTER(kvrec_cache), p, p, p, i64, i32, i32, p]
+    L.kvrec_qnorm_rope_insert.restype = ctypes.c_int
+    L.kvrec_expand_candidates.argtypes = [p, i64, p, i64, p, i64, i64, i32, i32, i32, p, i64, p,
+                                          i64, p]
+    L.kvrec_expand_candidates.restype = ctypes.c_int
     L.kvrec_gather.argtypes = [ctypes.POINTER(kvrec_cache), p, i64, p, p]
     L.kvrec_gather.restype = ctypes.c_int
     L.kvrec_status_str.argtypes = [ctypes.c_int]
@@ -274,6 +281,92 @@ def kvrec_insert_full(kv: torch.Tensor, k_cache: torch.Tensor, slot_mapping: tor
             kv.data_ptr(), n, ctypes.byref(desc), slot_mapping.data_ptr(), positions.data_ptr(),
             cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], int(block_size), rec, scale_p,
             _stream_handle(kv.device)))
+
+
+def kvrec_qnorm_rope_insert(q: torch.Tensor, kv: torch.Tensor, k_cache: torch.Tensor,
+                            slot_mapping: torch.Tensor, positions: torch.Tensor,
+                            cos_sin_cache: torch.Tensor, block_size: int, eps: float = 1e-6,
+                            apply_q_norm: bool = True, q_out: Optional[torch.Tensor] = None,
+                            record: Optional[int] = None) -> torch.Tensor:
+    """The attention write (the C ``kvrec_qnorm_rope_insert``): for every
+    token and head of ``q`` (bf16 ``[tokens, heads, 512]``), RMSNorm over the
+    head (if ``apply_q_norm``) and the NeoX rotation of its tail, written to
+    ``q_out`` (default: ``q`` itself, in place); and the KV insert of ``kv``
+    into the packed ``k_cache``, in one launch. Returns the q output."""
+    _check_insert_inputs(kv, k_cache, slot_mapping, positions, cos_sin_cache)
+    _require_gpu(q, "q")
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != HEAD_DIM or \
+            not q.is_contiguous():
+        raise TypeError("q must be contiguous bf16 [tokens, heads, 512]")
+    n = slot_mapping.shape[0]
+    if q.shape[0] < n:
+        raise ValueError("q must cover every token of slot_mapping")
+    if q.device != kv.device:
+        raise ValueError("q must be on kv's device")
+    if q_out is None:
+        q_out = q
+    else:
+        _require_gpu(q_out, "q_out")
+        if q_out.dtype != torch.bfloat16 or q_out.shape != q.shape or not q_out.is_contiguous():
+            raise ValueError(f"q_out must be contiguous bf16 {tuple(q.shape)}")
+        if q_out.device != q.device:
+            raise ValueError("q_out must be on q's device")
+    desc = cache_descriptor(k_cache)
+    rec = desc.record if record is None else int(record)
+    with torch.cuda.device(kv.device):
+        _check(load_library().kvrec_qnorm_rope_insert(
+            q.data_ptr(), q_out.data_ptr(), int(q.shape[1]), float(eps), int(bool(apply_q_norm)),
+            kv.data_ptr(), n, ctypes.byref(desc), slot_mapping.data_ptr(), positions.data_ptr(),
+            cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], int(block_size), rec,
+            _stream_handle(kv.device)))
+    return q_out
+
+
+def kvrec_expand_candidates(candidate_blocks: torch.Tensor, row_ks: torch.Tensor,
+                            row_ke: torch.Tensor, ratio: int, sparse_block: int,
+                            out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+                            ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The sparse indexer's candidate-block expansion (the C
+    ``kvrec_expand_candidates``; the page's candidate_blocks_to_sparse_indices):
+    int32 ``candidate_blocks [rows, K]`` (any row stride, unit column stride),
+    ``row_ks`` / ``row_ke`` int32 ``[rows]`` (any stride) -> ``(sparse_indices
+    [rows, K * ratio], end [rows])``, written into ``out`` when given."""
+    for name, t in (("candidate_blocks", candidate_blocks), ("row_ks", row_ks),
+                    ("row_ke", row_ke)):
+        _require_gpu(t, name)
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if candidate_blocks.dim() != 2 or candidate_blocks.stride(1) != 1:
+        raise ValueError("candidate_blocks must be [rows, K] with unit column stride")
+    rows, k = candidate_blocks.shape
+    if row_ks.dim() != 1 or row_ke.dim() != 1 or row_ks.shape[0] < rows or \
+            row_ke.shape[0] < rows:
+        raise ValueError("row_ks and row_ke must be 1-D and cover every row")
+    dev = candidate_blocks.device
+    if row_ks.device != dev or row_ke.device != dev:
+        raise ValueError("all tensors must be on one device")
+    width = k * int(ratio)
+    if out is None:
+        sparse = torch.empty((rows, width), dtype=torch.int32, device=dev)
+        end = torch.empty(rows, dtype=torch.int32, device=dev)
+    else:
+        sparse, end = out
+        _require_gpu(sparse, "sparse_indices")
+        _require_gpu(end, "end")
+        if sparse.dtype != torch.int32 or sparse.dim() != 2 or tuple(sparse.shape) != (rows, width) \
+                or sparse.stride(1) != 1 or end.dtype != torch.int32 or end.dim() != 1 or \
+                end.shape[0] < rows:
+            raise ValueError(f"out must be int32 ([{rows}, {width}] unit column stride, [{rows}])")
+        if sparse.device != dev or end.device != dev:
+            raise ValueError("out must be on the inputs' device")
+    with torch.cuda.device(dev):
+        _check(load_library().kvrec_expand_candidates(
+            candidate_blocks.data_ptr(), candidate_blocks.stride(0) if rows > 1 else k,
+            row_ks.data_ptr(), row_ks.stride(0), row_ke.data_ptr(), row_ke.stride(0), rows, k,
+            int(ratio), int(sparse_block), sparse.data_ptr(),
+            sparse.stride(0) if rows > 1 else width, end.data_ptr(), end.stride(0),
+            _stream_handle(dev)))
+    return sparse, end
 
 
 def kvrec_gather(k_cache: torch.Tensor, token_indices: torch.Tensor,

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libkvrec.so")
 ARCH = "gfx950"
 
-SOURCES = ["kvrec_kernels.hip", "kvrec_api.cpp"]
+SOURCES = ["kvrec_kernels.hip", "kvrec_expand.hip", "kvrec_api.cpp"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -22,6 +22,8 @@ namespace {
 
 constexpr int64_t kMaxCount = int64_t{1} << 30;  // rows and slots; keeps grids < 2^31 blocks
 constexpr int64_t kMaxPos = int64_t{1} << 30;    // cos/sin rows (a 256 GB table); pos + 1 < 2^31
+constexpr int32_t kMaxHeads = 1024;              // q heads of the attention write
+constexpr int32_t kMaxExpanded = 1024;           // K * RATIO of the candidate expansion
 
 bool misaligned(const void *p, uintptr_t align) {
   return (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0;
@@ -186,6 +188,47 @@ int kvrec_insert_full(const void *kv, int64_t num_tokens, const kvrec_cache *k_c
   return err == hipSuccess ? KVREC_OK : KVREC_ERR_HIP;
 }
 
+int kvrec_qnorm_rope_insert(const void *q_in, void *q_out, int32_t num_heads, float eps,
+                            int32_t apply_q_norm, const void *kv, int64_t num_tokens,
+                            const kvrec_cache *k_cache, const int64_t *slot_mapping,
+                            const int64_t *positions, const float *cos_sin_cache,
+                            int64_t max_pos, int32_t block_size, int32_t record,
+                            kvrec_stream stream) {
+  if (k_cache == nullptr) return KVREC_ERR_NULL;
+  if (!packed_record(record) || record != k_cache->record) return KVREC_ERR_RECORD;
+  if (block_size < 1 || block_size != k_cache->block_size) return KVREC_ERR_BLOCK_SIZE;
+  kvrec::CacheGeom g;
+  const int rc = check_cache(k_cache, &g);
+  if (rc != KVREC_OK) return rc;
+  if (apply_q_norm != 0 && apply_q_norm != 1) return KVREC_ERR_OPTION;
+  if (apply_q_norm == 1 && (!(eps > 0.0f) || !isfinite(eps))) return KVREC_ERR_OPTION;
+  if (num_heads < 1 || num_heads > kMaxHeads) return KVREC_ERR_SIZE;
+  if (num_tokens < 0 || num_tokens > kMaxCount / num_heads) return KVREC_ERR_SIZE;
+  if (num_tokens == 0) return KVREC_OK;
+  if (q_in == nullptr || q_out == nullptr || kv == nullptr || slot_mapping == nullptr ||
+      positions == nullptr || cos_sin_cache == nullptr)
+    return KVREC_ERR_NULL;
+  if (max_pos < 1 || max_pos > kMaxPos) return KVREC_ERR_SIZE;
+  if (misaligned(q_in, 16) || misaligned(q_out, 16) || misaligned(kv, 16) ||
+      misaligned(cos_sin_cache, 16) || misaligned(slot_mapping, 8) || misaligned(positions, 8))
+    return KVREC_ERR_ALIGNMENT;
+  // q_out is q_in (in place) or a separate buffer; a partial overlap would
+  // let one wave read rows another has already written.
+  const uintptr_t qi = reinterpret_cast<uintptr_t>(q_in), qo = reinterpret_cast<uintptr_t>(q_out);
+  const uintptr_t q_bytes = static_cast<uintptr_t>(num_tokens) * num_heads * KVREC_HEAD_DIM * 2;
+  if (qi != qo && qi < qo + q_bytes && qo < qi + q_bytes) return KVREC_ERR_OVERLAP;
+  kvrec::QArgs q;
+  q.in = q_in;
+  q.out = q_out;
+  q.heads = num_heads;
+  q.eps = apply_q_norm == 1 ? eps : 0.0f;
+  q.norm = apply_q_norm == 1;
+  const hipError_t err =
+      kvrec::launch_qkv(q, kv, num_tokens, g, slot_mapping, positions, cos_sin_cache, max_pos,
+                        record == KVREC_RECORD_LEGACY, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? KVREC_OK : KVREC_ERR_HIP;
+}
+
 int kvrec_gather(const kvrec_cache *k_cache, const int32_t *token_indices, int64_t num_indices,
                  void *out, kvrec_stream stream) {
   kvrec::CacheGeom g;
@@ -200,6 +243,51 @@ int kvrec_gather(const kvrec_cache *k_cache, const int32_t *token_indices, int64
   const hipError_t err = k_cache->record == KVREC_RECORD_MXFP8
                              ? kvrec::launch_gather_mxfp8(g, token_indices, num_indices, out, s)
                              : kvrec::launch_gather_legacy(g, token_indices, num_indices, out, s);
+  return err == hipSuccess ? KVREC_OK : KVREC_ERR_HIP;
+}
+
+int kvrec_expand_candidates(const int32_t *candidate_blocks, int64_t cand_stride,
+                            const int32_t *row_ks, int64_t ks_stride, const int32_t *row_ke,
+                            int64_t ke_stride, int64_t rows, int32_t num_candidates,
+                            int32_t ratio, int32_t sparse_block, int32_t *sparse_indices,
+                            int64_t sparse_stride, int32_t *end, int64_t end_stride,
+                            kvrec_stream stream) {
+  // The page's kernel takes K a power of two, RATIO 1 or 2 and SBK 16 or 8
+  // (the block sizes its sparse attention accepts).
+  if (num_candidates < 1 || num_candidates > kMaxExpanded ||
+      (num_candidates & (num_candidates - 1)) != 0)
+    return KVREC_ERR_SIZE;
+  if (ratio != 1 && ratio != 2) return KVREC_ERR_OPTION;
+  if (sparse_block != 8 && sparse_block != 16) return KVREC_ERR_OPTION;
+  const int64_t width = static_cast<int64_t>(num_candidates) * ratio;
+  if (width > kMaxExpanded) return KVREC_ERR_SIZE;
+  if (rows < 0 || rows > kMaxCount) return KVREC_ERR_SIZE;
+  if (cand_stride < num_candidates || sparse_stride < width || ks_stride < 1 ||
+      ke_stride < 1 || end_stride < 1)
+    return KVREC_ERR_SIZE;
+  if (rows == 0) return KVREC_OK;
+  if (candidate_blocks == nullptr || row_ks == nullptr || row_ke == nullptr ||
+      sparse_indices == nullptr || end == nullptr)
+    return KVREC_ERR_NULL;
+  if (misaligned(candidate_blocks, 4) || misaligned(row_ks, 4) || misaligned(row_ke, 4) ||
+      misaligned(sparse_indices, 4) || misaligned(end, 4))
+    return KVREC_ERR_ALIGNMENT;
+  kvrec::ExpandArgs x;
+  x.cand = candidate_blocks;
+  x.cand_stride = cand_stride;
+  x.ks = row_ks;
+  x.ks_stride = ks_stride;
+  x.ke = row_ke;
+  x.ke_stride = ke_stride;
+  x.rows = rows;
+  x.num_candidates = num_candidates;
+  x.ratio = ratio;
+  x.sparse_block = sparse_block;
+  x.sparse = sparse_indices;
+  x.sparse_stride = sparse_stride;
+  x.end = end;
+  x.end_stride = end_stride;
+  const hipError_t err = kvrec::launch_expand(x, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? KVREC_OK : KVREC_ERR_HIP;
 }
 
@@ -218,6 +306,7 @@ const char *kvrec_status_str(int status) {
     case KVREC_ERR_SIZE: return "size out of range";
     case KVREC_ERR_HIP: return "HIP launch error";
     case KVREC_ERR_OPTION: return "insert option out of range";
+    case KVREC_ERR_OVERLAP: return "output buffer partly overlaps an input";
     default: return "unknown kvrec status";
   }
 }

@@ -146,14 +146,11 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4 w, float f[8]) {
   f[7] = __uint_as_float(w.w & 0xFFFF0000u);
 }
 
-// bf16 bits nearest to a finite fp32 value, ties to even.
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  const uint32_t b = __float_as_uint(x);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
+// bf16 bits nearest to two finite fp32 values, ties to even (lo in the low
+// half): one v_cvt_pk_bf16_f32, which rounds in the wave's round-to-nearest-
+// even mode and keeps fp32 denormals (the kernels run with them enabled).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 template <int Ctrl>
@@ -231,8 +228,13 @@ __device__ __forceinline__ u32x2 encode_e4m3x8(const float f[8], uint32_t scale_
 //   lanes 56..59 hold x1 = dims 448+i, lanes 60..63 hold x2 = dims 480+i,
 //   i = 8*(lane & 3) + k; cos = row[i], sin = row[32 + i].
 //   r1 = x1*c - x2*s,  r2 = x2*c + x1*s  (each operation rounded separately)
+//   With kScaled, the values are x * inv (the q side's normalised rows): the
+//   partner's raw bf16 values are multiplied by the same inv, exactly as the
+//   partner lane scales its own.
+template <bool kScaled = false>
 __device__ __forceinline__ void rope_tail(float f[8], const u32x4 raw, int lane, const f32x4 c0,
-                                          const f32x4 c1, const f32x4 s0, const f32x4 s1) {
+                                          const f32x4 c1, const f32x4 s0, const f32x4 s1,
+                                          float inv = 1.0f) {
   u32x4 pr;
   pr.x = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(raw.x), kSwizzleXor4));
   pr.y = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(raw.y), kSwizzleXor4));
@@ -241,6 +243,10 @@ __device__ __forceinline__ void rope_tail(float f[8], const u32x4 raw, int lane,
   if (lane >= 56) {
     float g[8];
     unpack_bf16x8(pr, g);
+    if constexpr (kScaled) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) g[k] = g[k] * inv;
+    }
     const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
     const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
     const bool second = (lane & 4) != 0;  // this lane holds x2 (dims 480..)
@@ -382,6 +388,28 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
   }
 }
 
+// Lanes 56..63 read the cos/sin values of table row `row` that they use:
+// NeoX lane 56+j takes cos[8(j&3) .. +7] and sin[8(j&3) .. +7]; interleaved
+// lane 56+j takes cos[4j .. 4j+3] and sin[4j .. 4j+3]. Other lanes load
+// nothing.
+template <int P, int kRope>
+__device__ __forceinline__ void load_table(const f32x4 *cos_sin, uint32_t row, int lane,
+                                           f32x4 &c0, f32x4 &c1, f32x4 &s0, f32x4 &s1) {
+  if (kRope == kRopeNone || lane < 56) return;
+  const f32x4 *tab = cos_sin + static_cast<uint64_t>(row) * 16;
+  constexpr bool nt = (P & kNtTable) != 0;
+  if constexpr (kRope == kRopeNeox) {
+    const int q = 2 * (lane & 3);  // float4 index of cos[8*(lane&3)]
+    c0 = ld<nt>(tab + q);
+    c1 = ld<nt>(tab + q + 1);
+    s0 = ld<nt>(tab + 8 + q);
+    s1 = ld<nt>(tab + 9 + q);
+  } else {
+    c0 = ld<nt>(tab + (lane - 56));      // cos of pairs 4j..4j+3
+    s0 = ld<nt>(tab + 8 + (lane - 56));  // sin of the same pairs
+  }
+}
+
 // Insert: wave w of block b handles tokens T*(W*b + w) .. +T-1. For all of
 // them it first issues the loads that depend on nothing (kv rows, slots,
 // positions), then the cos/sin rows (which need the positions), and only
@@ -393,6 +421,74 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
 // saves each wave a dependent kernarg load before its first memory request.
 // kOptions = false is the plain insert (NeoX, ratio 1, no floor, positions
 // present); its code carries none of the option checks below.
+// One wave's share of the insert: tokens t0 .. t0+T-1 (t0 < n).
+template <int P, int T, int kFmt, int kRope, bool kSanitize, bool kOptions>
+__device__ __forceinline__ void insert_wave(const InsertArgs &a, uint32_t t0, int lane,
+                                            uint32_t ratio, uint32_t ratio_magic,
+                                            uint32_t ratio_shift, uint32_t amax_floor_bits,
+                                            float scale) {
+  // With a compression ratio above 1 most tokens are gated off, so the kv
+  // row is read only once the gate has passed; otherwise it is read at once,
+  // beside the slot and position.
+  const bool defer = kOptions && ratio > 1;
+  // No positions: only the rotation-free insert with ratio 1 (host-checked).
+  const bool has_pos = !kOptions || a.positions != nullptr;
+  u32x4 raw[T];
+  int64_t sl[T], ps[T];
+#pragma unroll
+  for (int k = 0; k < T; ++k) {
+    const uint32_t t = t0 + k;
+    const bool in = (T == 1) || t < a.n;
+    raw[k] = in && !defer
+                 ? ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t) * kWave + lane)
+                 : u32x4{0, 0, 0, 0};
+    sl[k] = in ? a.slots[t] : -1;
+    ps[k] = !has_pos ? 0 : in ? a.positions[t] : -1;
+  }
+  // All three loads are issued before anything waits on the slot or position.
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t slot[T], row[T];
+  bool ok[T];
+#pragma unroll
+  for (int k = 0; k < T; ++k) {
+    ok[k] = below(sl[k], a.total_slots) && (!has_pos || below(ps[k], a.max_pos));
+    slot[k] = static_cast<uint32_t>(sl[k]);
+    row[k] = static_cast<uint32_t>(ps[k]);
+    if (kOptions && ratio > 1) {
+      // Compressed-KV gate ([MXFP8 record] 关键源码片段): write only when
+      // (pos + 1) % ratio == 0, rotating with row pos / ratio * ratio, which
+      // is then pos + 1 - ratio. pos + 1 <= 2^30, so the division is exact.
+      const uint32_t p1 = row[k] + 1;
+      const uint32_t q = (__umulhi(p1, ratio_magic) + p1) >> ratio_shift;
+      ok[k] = ok[k] && p1 == q * ratio;
+      row[k] = p1 - ratio;
+      if (ok[k])
+        raw[k] = ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t0 + k) * kWave + lane);
+    }
+  }
+  // The kv row is used only on the encode path; left to itself the compiler
+  // sinks its load there, behind the wait for the slot and position. An
+  // empty asm reading it on the skip path too keeps the load at the top, in
+  // flight together with the slot and position loads.
+#pragma unroll
+  for (int k = 0; k < T; ++k)
+    if (!defer && !ok[k]) asm volatile("" ::"v"(raw[k]));
+  // Only lanes 56..63 read (and later use) the cos/sin values. The empty asm
+  // statements give the registers an unset value in the other lanes, so the
+  // compiler does not spend moves per token zero-filling them.
+  f32x4 c0[T], c1[T], s0[T], s1[T];
+#pragma unroll
+  for (int k = 0; k < T; ++k) {
+    asm("" : "=v"(c0[k]), "=v"(c1[k]), "=v"(s0[k]), "=v"(s1[k]));
+    if (ok[k]) load_table<P, kRope>(a.cos_sin, row[k], lane, c0[k], c1[k], s0[k], s1[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < T; ++k)
+    if (ok[k])
+      encode_store<P, kFmt, kRope, kSanitize, kOptions>(a, lane, raw[k], c0[k], c1[k], s0[k],
+                                                        s1[k], slot[k], amax_floor_bits, scale);
+}
+
 template <int P, int W, int T, int kFmt, int kRope, bool kSanitize, bool kOptions>
 __global__ __launch_bounds__(W * kWave) void insert_kernel(
     uint32_t n, uint32_t per_xcd, const u32x4 *kv, const int64_t *slots, const int64_t *positions,
@@ -409,67 +505,159 @@ __global__ __launch_bounds__(W * kWave) void insert_kernel(
   // The per-tensor scale of the fp8 cache: one uniform load per wave.
   float scale = 1.0f;
   if constexpr (kFmt == kFmtFp8) scale = *fp8_scale;
+  insert_wave<P, T, kFmt, kRope, kSanitize, kOptions>(a, t0, lane, ratio, ratio_magic,
+                                                      ratio_shift, amax_floor_bits, scale);
+}
 
-  // With a compression ratio above 1 most tokens are gated off, so the kv
-  // row is read only once the gate has passed; otherwise it is read at once,
-  // beside the slot and position.
-  const bool defer = kOptions && ratio > 1;
-  u32x4 raw[T];
-  uint32_t slot[T], row[T];
-  bool ok[T];
+// Sum of a value over the 64 lanes, returned in every lane. Each step adds a
+// partner lane's value (a + b == b + a in IEEE arithmetic, so every lane ends
+// with the same bits): quad xor 1, quad xor 2, 8-lane mirror, 16-lane mirror,
+// then lanes 16 and 32 apart.
+constexpr int kRowMirror = 0x140;  // lane i <-> 15-i within 16 lanes
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = v + __uint_as_float(dpp<kQuadXor1>(__float_as_uint(v)));
+  v = v + __uint_as_float(dpp<kQuadXor2>(__float_as_uint(v)));
+  v = v + __uint_as_float(dpp<kHalfRowMirror>(__float_as_uint(v)));
+  v = v + __uint_as_float(dpp<kRowMirror>(__float_as_uint(v)));
+  const int lane = threadIdx.x & (kWave - 1);
+  v = v + __uint_as_float(lane_read(__float_as_uint(v), lane ^ 16));
+  v = v + __uint_as_float(lane_read(__float_as_uint(v), lane ^ 32));
+  return v;
+}
+
+// q side of the attention write for heads h0 .. h0+HPW-1 (those < heads) of
+// token t (the QNorm op of [KV-only op] 实现拆解 1; readings: a weightless
+// RMSNorm over the head's 512 dims, then the NeoX rotation of the tail with
+// the token's table row). Per head: lane l holds dims 8l..8l+7; the sum of
+// squares is formed in fp32 (lane-local products and sums, then wave_sum),
+// inv = rsq(sum / 512 + eps) (v_rsq_f32, within 1 ulp), y = x * inv, then the
+// rotation and round-to-nearest-even bf16. A token whose position is out of
+// range leaves its rows unwritten.
+template <int P, int HPW, bool kNorm>
+__device__ __forceinline__ void qnorm_rope_wave(const InsertArgs &a, const u32x4 *q_in,
+                                                u32x4 *q_out, uint32_t t, uint32_t h0,
+                                                uint32_t heads, int lane, float eps) {
+  const int64_t ps = a.positions[t];
+  if (!below(ps, a.max_pos)) return;
+  f32x4 c0, c1, s0, s1;
+  asm("" : "=v"(c0), "=v"(c1), "=v"(s0), "=v"(s1));
+  load_table<P, kRopeNeox>(a.cos_sin, static_cast<uint32_t>(ps), lane, c0, c1, s0, s1);
+  const uint64_t row0 = static_cast<uint64_t>(t) * heads + h0;
+  u32x4 raw[HPW];
 #pragma unroll
-  for (int k = 0; k < T; ++k) {
-    const uint32_t t = t0 + k;
-    const bool in = (T == 1) || t < a.n;
-    raw[k] = in && !defer
-                 ? ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t) * kWave + lane)
-                 : u32x4{0, 0, 0, 0};
-    const int64_t sl = in ? a.slots[t] : -1;
-    // No positions: only the rotation-free insert with ratio 1 (host-checked).
-    const bool has_pos = !kOptions || positions != nullptr;
-    const int64_t ps = !has_pos ? 0 : in ? a.positions[t] : -1;
-    ok[k] = below(sl, a.total_slots) && (!has_pos || below(ps, a.max_pos));
-    slot[k] = static_cast<uint32_t>(sl);
-    row[k] = static_cast<uint32_t>(ps);
-    if (kOptions && ratio > 1) {
-      // Compressed-KV gate ([MXFP8 record] 关键源码片段): write only when
-      // (pos + 1) % ratio == 0, rotating with row pos / ratio * ratio, which
-      // is then pos + 1 - ratio. pos + 1 <= 2^30, so the division is exact.
-      const uint32_t p1 = row[k] + 1;
-      const uint32_t q = (__umulhi(p1, ratio_magic) + p1) >> ratio_shift;
-      ok[k] = ok[k] && p1 == q * ratio;
-      row[k] = p1 - ratio;
-      if (ok[k])
-        raw[k] = ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t0 + k) * kWave + lane);
+  for (int k = 0; k < HPW; ++k)
+    if (h0 + k < heads) raw[k] = ld<(P & kNtKv) != 0>(q_in + (row0 + k) * kWave + lane);
+#pragma unroll
+  for (int k = 0; k < HPW; ++k) {
+    if (h0 + k >= heads) break;
+    float f[8];
+    unpack_bf16x8(raw[k], f);
+    float inv = 1.0f;
+    if constexpr (kNorm) {
+      float ss = f[0] * f[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) ss = ss + f[j] * f[j];
+      ss = wave_sum(ss);
+      inv = __builtin_amdgcn_rsqf(ss * (1.0f / 512.0f) + eps);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = f[j] * inv;
     }
+    rope_tail<kNorm>(f, raw[k], lane, c0, c1, s0, s1, inv);
+    u32x4 h;
+    h.x = pack_bf16x2(f[0], f[1]);
+    h.y = pack_bf16x2(f[2], f[3]);
+    h.z = pack_bf16x2(f[4], f[5]);
+    h.w = pack_bf16x2(f[6], f[7]);
+    q_out[(row0 + k) * kWave + lane] = h;
   }
-  // Only lanes 56..63 read (and later use) the cos/sin values. The empty asm
-  // statements give the registers an unset value in the other lanes, so the
-  // compiler does not spend moves per token zero-filling them.
-  f32x4 c0[T], c1[T], s0[T], s1[T];
-#pragma unroll
-  for (int k = 0; k < T; ++k) {
-    asm("" : "=v"(c0[k]), "=v"(c1[k]), "=v"(s0[k]), "=v"(s1[k]));
-    if (kRope != kRopeNone && ok[k] && lane >= 56) {
-      const f32x4 *tab = a.cos_sin + static_cast<uint64_t>(row[k]) * 16;
-      constexpr bool nt = (P & kNtTable) != 0;
-      if constexpr (kRope == kRopeNeox) {
-        const int q = 2 * (lane & 3);  // float4 index of cos[8*(lane&3)]
-        c0[k] = ld<nt>(tab + q);
-        c1[k] = ld<nt>(tab + q + 1);
-        s0[k] = ld<nt>(tab + 8 + q);
-        s1[k] = ld<nt>(tab + 9 + q);
-      } else {
-        c0[k] = ld<nt>(tab + (lane - 56));      // cos of pairs 4j..4j+3
-        s0[k] = ld<nt>(tab + 8 + (lane - 56));  // sin of the same pairs
-      }
-    }
+}
+
+// The attention write: the q side for every (token, head group) and the KV
+// insert for every token, in one launch. Waves [0, q_waves) take head group
+// w % wpt of token w / wpt; waves [q_waves, q_waves + n) take one token's
+// insert each.
+template <int P, int kFmt, int HPW, bool kNorm>
+__global__ __launch_bounds__(kWave) void qkv_kernel(
+    uint32_t n, uint32_t per_xcd, const u32x4 *kv, const int64_t *slots, const int64_t *positions,
+    const f32x4 *cos_sin, uint32_t max_pos, uint32_t total_slots, uint8_t *base,
+    int64_t page_stride, uint32_t block_size, uint32_t div_magic, uint32_t div_shift,
+    const u32x4 *q_in, u32x4 *q_out, uint32_t heads, uint32_t q_waves, uint32_t wpt,
+    uint32_t wpt_magic, uint32_t wpt_shift, float eps) {
+  const InsertArgs a{kv,         slots,       positions, cos_sin,   base,    page_stride, n,
+                     block_size, total_slots, div_magic, div_shift, max_pos};
+  const int lane = threadIdx.x;
+  const uint32_t w = xcd_block(per_xcd);
+  if (w < q_waves) {
+    const uint32_t t = (__umulhi(w, wpt_magic) + w) >> wpt_shift;
+    qnorm_rope_wave<P, HPW, kNorm>(a, q_in, q_out, t, (w - t * wpt) * HPW, heads, lane, eps);
+    return;
   }
-#pragma unroll
-  for (int k = 0; k < T; ++k)
-    if (ok[k])
-      encode_store<P, kFmt, kRope, kSanitize, kOptions>(a, lane, raw[k], c0[k], c1[k], s0[k],
-                                                        s1[k], slot[k], amax_floor_bits, scale);
+  const uint32_t t0 = w - q_waves;
+  if (t0 >= a.n) return;
+  insert_wave<P, 1, kFmt, kRopeNeox, false, false>(a, t0, lane, 1, 0, 0, 0, 1.0f);
+}
+
+// The compressed-KV insert with a ratio R > 1 ([MXFP8 record] 关键源码片段)
+// writes one token in R. One wave per token would spend most waves on a
+// slot/position round trip and nothing else, so here each wave takes a
+// group of `group` (<= 64) consecutive tokens: lane j reads the slot and
+// position of token j of the group and evaluates the gate, a ballot collects
+// the kept tokens, and the wave then encodes only those, two at a time so
+// that their kv and table loads are in flight together (a group holds about
+// two kept tokens, see gated_group). The work per kept
+// token (and every byte written) is that of insert_kernel.
+template <int P, int kFmt, int kRope, bool kSanitize>
+__global__ __launch_bounds__(kWave) void insert_gated_kernel(
+    uint32_t n, uint32_t per_xcd, const u32x4 *kv, const int64_t *slots, const int64_t *positions,
+    const f32x4 *cos_sin, uint32_t max_pos, uint32_t total_slots, uint8_t *base,
+    int64_t page_stride, uint32_t block_size, uint32_t div_magic, uint32_t div_shift,
+    uint32_t ratio, uint32_t ratio_magic, uint32_t ratio_shift, uint32_t amax_floor_bits,
+    uint32_t group) {
+  const InsertArgs a{kv,         slots,       positions, cos_sin,   base,    page_stride, n,
+                     block_size, total_slots, div_magic, div_shift, max_pos};
+  const int lane = threadIdx.x;
+  const uint32_t t0 = xcd_block(per_xcd) * group;
+  if (t0 >= a.n) return;
+
+  bool ok = false;
+  uint32_t slot = 0, row = 0;
+  if (static_cast<uint32_t>(lane) < group && t0 + lane < a.n) {
+    const int64_t sl = ld<(P & kNtKv) != 0>(a.slots + t0 + lane);
+    const int64_t ps = ld<(P & kNtKv) != 0>(a.positions + t0 + lane);
+    // (pos + 1) % R == 0, rotating with row pos / R * R = pos + 1 - R;
+    // pos + 1 <= 2^30, so the magic-number division is exact.
+    const uint32_t p1 = static_cast<uint32_t>(ps) + 1;
+    const uint32_t q = (__umulhi(p1, ratio_magic) + p1) >> ratio_shift;
+    ok = below(sl, a.total_slots) && below(ps, a.max_pos) && p1 == q * ratio;
+    slot = static_cast<uint32_t>(sl);
+    row = p1 - ratio;
+  }
+  uint64_t kept = __ballot(ok);
+  while (kept != 0) {
+    const int k0 = __builtin_ctzll(kept);
+    kept &= kept - 1;
+    const bool two = kept != 0;
+    const int k1 = two ? __builtin_ctzll(kept) : k0;
+    if (two) kept &= kept - 1;
+    const uint32_t slot0 = __builtin_amdgcn_readlane(slot, k0);
+    const uint32_t row0 = __builtin_amdgcn_readlane(row, k0);
+    const uint32_t slot1 = __builtin_amdgcn_readlane(slot, k1);
+    const uint32_t row1 = __builtin_amdgcn_readlane(row, k1);
+    constexpr bool nt_kv = (P & kNtKv) != 0;
+    const u32x4 raw0 = ld<nt_kv>(a.kv + static_cast<uint64_t>(t0 + k0) * kWave + lane);
+    const u32x4 raw1 = ld<nt_kv>(a.kv + static_cast<uint64_t>(t0 + k1) * kWave + lane);
+    f32x4 c0, c1, s0, s1, d0, d1, e0, e1;
+    asm("" : "=v"(c0), "=v"(c1), "=v"(s0), "=v"(s1));
+    asm("" : "=v"(d0), "=v"(d1), "=v"(e0), "=v"(e1));
+    load_table<P, kRope>(a.cos_sin, row0, lane, c0, c1, s0, s1);
+    load_table<P, kRope>(a.cos_sin, row1, lane, d0, d1, e0, e1);
+    encode_store<P, kFmt, kRope, kSanitize, true>(a, lane, raw0, c0, c1, s0, s1, slot0,
+                                                  amax_floor_bits, 1.0f);
+    if (two)
+      encode_store<P, kFmt, kRope, kSanitize, true>(a, lane, raw1, d0, d1, e0, e1, slot1,
+                                                    amax_floor_bits, 1.0f);
+  }
 }
 
 // bf16 of e4m3fn(code) * 2^(scale_byte - 127) for 8 codes, value k = byte k.
@@ -556,6 +744,19 @@ constexpr int kInsertWaves = 1;   // waves per block
 constexpr int kInsertTokens = 1;  // tokens per wave
 constexpr int kGatherPolicy = kNtOut;
 constexpr int kGatherWaves = 2;
+// q rows (heads) per wave of the attention write. Measured on MI355X at 4096
+// tokens x 128 heads, back to back: 1, 2, 4 and 8 heads per wave took 216,
+// 180, 188 and 203 us.
+constexpr int kQHeadsPerWave = 2;
+
+// Granlund-Montgomery magic for a divisor d >= 1 (as on the host): for every
+// n < 2^31, n / d == (umulhi(n, magic) + n) >> shift.
+void division_magic32(uint32_t d, uint32_t *magic, uint32_t *shift) {
+  uint32_t l = 0;
+  while ((uint64_t{1} << l) < d) ++l;
+  *magic = static_cast<uint32_t>(((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1);
+  *shift = l;
+}
 constexpr int kGatherRows = 2;    // rows per wave
 
 // Grid of `waves` waves in blocks of W, padded to a whole number of blocks
@@ -590,6 +791,36 @@ hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const in
       dim3(W * kWave), params, 0, stream);
 }
 
+// Tokens per wave of the gated kernel: about two kept tokens per group, i.e.
+// one round of loads per wave (measured on MI355X at the 262144-token prefill
+// shape: groups of R, 2R, 4R and 8R tokens took 33.6, 26.5, 27.8 and 30.0 us
+// at R = 4).
+uint32_t gated_group(uint32_t ratio) { return ratio >= 32 ? 64u : 2u * ratio; }
+
+template <int kFmt, int kRope, bool kSanitize>
+hipError_t launch_insert_gated(const void *kv, int64_t n, const CacheGeom &g,
+                               const int64_t *slots, const int64_t *positions,
+                               const float *cos_sin, int64_t max_pos, const InsertOptions &o,
+                               hipStream_t stream) {
+  uint32_t group = gated_group(o.ratio);
+  uint32_t per_xcd = 0;
+  const dim3 grid = xcd_grid<1>((n + group - 1) / group, &per_xcd);
+  uint32_t n32 = static_cast<uint32_t>(n), mp = static_cast<uint32_t>(max_pos);
+  const u32x4 *kv4 = static_cast<const u32x4 *>(kv);
+  const f32x4 *cs4 = reinterpret_cast<const f32x4 *>(cos_sin);
+  uint8_t *base = g.base;
+  int64_t stride = g.page_stride;
+  uint32_t total = g.total_slots, bs = g.block_size, magic = g.div_magic, shift = g.div_shift;
+  uint32_t ratio = o.ratio, rmagic = o.ratio_magic, rshift = o.ratio_shift;
+  uint32_t floor_bits = o.amax_floor_bits;
+  void *params[] = {&n32,  &per_xcd, &kv4,  &slots, &positions, &cs4,   &mp,
+                    &total, &base,    &stride, &bs,   &magic,     &shift, &ratio,
+                    &rmagic, &rshift, &floor_bits, &group};
+  return hipLaunchKernel(
+      reinterpret_cast<const void *>(insert_gated_kernel<kInsertPolicy, kFmt, kRope, kSanitize>),
+      grid, dim3(kWave), params, 0, stream);
+}
+
 template <int kFmt, int kRope, bool kSanitize, bool kOptions = true>
 hipError_t launch_insert_tuned(const void *kv, int64_t n, const CacheGeom &g,
                                const int64_t *slots, const int64_t *positions,
@@ -615,7 +846,49 @@ hipError_t launch_gather(const CacheGeom &g, const int32_t *indices, int64_t n, 
                          dim3(W * kWave), params, 0, stream);
 }
 
+template <int kFmt, bool kNorm>
+hipError_t launch_qkv_t(const QArgs &q, const void *kv, int64_t n, const CacheGeom &g,
+                        const int64_t *slots, const int64_t *positions, const float *cos_sin,
+                        int64_t max_pos, hipStream_t stream) {
+  uint32_t wpt = static_cast<uint32_t>((q.heads + kQHeadsPerWave - 1) / kQHeadsPerWave);
+  uint32_t q_waves = static_cast<uint32_t>(n) * wpt;
+  uint32_t per_xcd = 0;
+  const dim3 grid = xcd_grid<1>(static_cast<int64_t>(q_waves) + n, &per_xcd);
+  uint32_t n32 = static_cast<uint32_t>(n), mp = static_cast<uint32_t>(max_pos);
+  const u32x4 *kv4 = static_cast<const u32x4 *>(kv);
+  const f32x4 *cs4 = reinterpret_cast<const f32x4 *>(cos_sin);
+  uint8_t *base = g.base;
+  int64_t stride = g.page_stride;
+  uint32_t total = g.total_slots, bs = g.block_size, magic = g.div_magic, shift = g.div_shift;
+  const u32x4 *qi = static_cast<const u32x4 *>(q.in);
+  u32x4 *qo = static_cast<u32x4 *>(q.out);
+  uint32_t heads = static_cast<uint32_t>(q.heads);
+  uint32_t wmagic = 0, wshift = 0;
+  division_magic32(wpt, &wmagic, &wshift);
+  float eps = q.eps;
+  void *params[] = {&n32,  &per_xcd, &kv4,   &slots, &positions, &cs4, &mp,      &total,
+                    &base, &stride,  &bs,    &magic, &shift,     &qi,  &qo,      &heads,
+                    &q_waves, &wpt,  &wmagic, &wshift, &eps};
+  return hipLaunchKernel(
+      reinterpret_cast<const void *>(qkv_kernel<kInsertPolicy, kFmt, kQHeadsPerWave, kNorm>),
+      grid, dim3(kWave), params, 0, stream);
+}
+
 }  // namespace
+
+hipError_t launch_qkv(const QArgs &q, const void *kv, int64_t n, const CacheGeom &g,
+                      const int64_t *slots, const int64_t *positions, const float *cos_sin,
+                      int64_t max_pos, bool legacy, hipStream_t stream) {
+  if (legacy)
+    return q.norm ? launch_qkv_t<kFmtLegacy, true>(q, kv, n, g, slots, positions, cos_sin,
+                                                   max_pos, stream)
+                  : launch_qkv_t<kFmtLegacy, false>(q, kv, n, g, slots, positions, cos_sin,
+                                                    max_pos, stream);
+  return q.norm ? launch_qkv_t<kFmtMxfp8, true>(q, kv, n, g, slots, positions, cos_sin, max_pos,
+                                                stream)
+                : launch_qkv_t<kFmtMxfp8, false>(q, kv, n, g, slots, positions, cos_sin, max_pos,
+                                                 stream);
+}
 
 hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
                          const int64_t *positions, const float *cos_sin, int64_t max_pos,
@@ -639,8 +912,11 @@ hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const in
   const bool legacy = format == Format::kLegacy;
 #define KVREC_INSERT(L, R, S)                                                                   \
   if (legacy == (L == kFmtLegacy) && o.rope == R && o.sanitize == S)                            \
-    return launch_insert_tuned<L, R, S>(kv, n, g, slots, positions, cos_sin, max_pos, o, nullptr, \
-                                        stream);
+    return o.ratio > 1                                                                          \
+               ? launch_insert_gated<L, R, S>(kv, n, g, slots, positions, cos_sin, max_pos, o,  \
+                                              stream)                                           \
+               : launch_insert_tuned<L, R, S>(kv, n, g, slots, positions, cos_sin, max_pos, o,  \
+                                              nullptr, stream);
 #define KVREC_INSERT_R(L, R) KVREC_INSERT(L, R, false) KVREC_INSERT(L, R, true)
 #define KVREC_INSERT_L(L) \
   KVREC_INSERT_R(L, kRopeNeox) KVREC_INSERT_R(L, kRopeInterleaved) KVREC_INSERT_R(L, kRopeNone)

@@ -38,6 +38,40 @@ hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const in
                          const int64_t *positions, const float *cos_sin, int64_t max_pos,
                          Format format, const InsertOptions &o, const float *fp8_scale,
                          hipStream_t stream);
+// q side of the attention write: bf16 [n, heads, 512] rows in and out (out
+// may be in), normalised with eps when norm is set.
+struct QArgs {
+  const void *in;
+  void *out;
+  int64_t heads;
+  float eps;
+  bool norm;
+};
+
+// The attention write: the q side plus the plain insert into a packed cache,
+// in one launch.
+hipError_t launch_qkv(const QArgs &q, const void *kv, int64_t n, const CacheGeom &g,
+                      const int64_t *slots, const int64_t *positions, const float *cos_sin,
+                      int64_t max_pos, bool legacy, hipStream_t stream);
+// Candidate-block expansion of the sparse indexer (kvrec_expand.hip).
+struct ExpandArgs {
+  const int32_t *cand;
+  int64_t cand_stride;
+  const int32_t *ks;
+  int64_t ks_stride;
+  const int32_t *ke;
+  int64_t ke_stride;
+  int64_t rows;
+  int32_t num_candidates;  // K, a power of two; K * ratio <= 1024
+  int32_t ratio;           // 1 or 2
+  int32_t sparse_block;    // SBK
+  int32_t *sparse;
+  int64_t sparse_stride;
+  int32_t *end;
+  int64_t end_stride;
+};
+
+hipError_t launch_expand(const ExpandArgs &x, hipStream_t stream);
 hipError_t launch_gather_mxfp8(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
                                hipStream_t stream);
 hipError_t launch_gather_legacy(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,

@@ -21,6 +21,10 @@ tokens, [KV-only op, 实现拆解 4 and 5]):
 * ``legacy_65536``   65536 tokens into the 584 B legacy record.
 * ``topk_gather``    a 32768-page MXFP8 cache filled in slot order; 64 queries
                      gather 2048 sorted indices each with 3% set to -1.
+* ``attention_write`` 4096 tokens x 128 q heads normalised and rotated, with
+                     the KV insert of the same tokens.
+* ``sparse_expand``  16384 query rows (4 causal sequences of 4096) expanding
+                     up to 128 candidate blocks each into sparse block indices.
 """
 from __future__ import annotations
 
@@ -260,6 +264,74 @@ def custom_insert(seed: int, n: int, record: int, block_size: int, num_blocks: i
         num_blocks=num_blocks, page_stride=stride, kv_bits=to_bf16_bits(x), slot_mapping=slots,
         positions=positions, cos_sin=rope_table(max_pos), backing_seed=seed + 100,
         gather_indices=slots.astype(np.int32))
+
+
+@dataclasses.dataclass
+class AttentionWrite:
+    """The attention write: q rows of every head plus the KV insert."""
+
+    name: str
+    q_bits: np.ndarray  # uint16 [n, heads, 512] (bf16 bits)
+    eps: float
+    insert: InsertCase
+
+
+def attention_write(seed: int = 1006, n: int = 4096, heads: int = 128,
+                    block_size: int = 64, eps: float = 1e-6) -> AttentionWrite:
+    """A prefill chunk of n tokens through the attention write: q is N(0,1)
+    times a per-(token, head) U(0.1, 10) with 1% of the heads all +0; the KV
+    part is ``prefill``-like (positions 0.., slots 0.., N(0,1) rows with 0.5%
+    of channels x300). The pages give no q shapes: 128 heads stands for a
+    padded head count."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((n, heads, HEAD_DIM), dtype=np.float32)
+    q *= rng.uniform(0.1, 10.0, (n, heads, 1)).astype(np.float32)
+    zero = rng.random((n, heads)) < 0.01
+    q[zero] = 0.0
+    x = rng.standard_normal((n, HEAD_DIM), dtype=np.float32)
+    chans = rng.choice(HEAD_DIM, int(round(0.005 * HEAD_DIM)), replace=False)
+    x[:, chans] *= 300.0
+    num_blocks = (n + block_size - 1) // block_size
+    case = InsertCase(
+        name=f"attention_write_{n}x{heads}", record=RECORD_MXFP8, block_size=block_size,
+        num_blocks=num_blocks, page_stride=page_stride_for(RECORD_MXFP8, block_size),
+        kv_bits=to_bf16_bits(x), slot_mapping=np.arange(n, dtype=np.int64),
+        positions=np.arange(n, dtype=np.int64), cos_sin=rope_table(n), backing_seed=seed + 100)
+    return AttentionWrite(case.name, to_bf16_bits(q), eps, case)
+
+
+@dataclasses.dataclass
+class SparseExpand:
+    """Inputs of the sparse indexer's candidate-block expansion."""
+
+    name: str
+    cand: np.ndarray    # int32 [rows, K]
+    row_ks: np.ndarray  # int32 [rows]
+    row_ke: np.ndarray  # int32 [rows]
+    ratio: int
+    sparse_block: int
+
+
+def sparse_expand(seed: int = 1007, seqs: int = 4, seq_len: int = 4096, k: int = 128,
+                  ratio: int = 2, sparse_block: int = 8) -> SparseExpand:
+    """A prefill chunk through the sparse indexer's expansion: `seqs`
+    sequences of `seq_len` query tokens laid end to end in the chunk's KV, so
+    row i of sequence s sees [s*seq_len, s*seq_len + i + 1) (causal). Its
+    candidates are up to K distinct candidate blocks of ratio*sparse_block
+    tokens drawn from those it can see, in random (score) order, padded with
+    -1 when fewer exist: 2048 top-k tokens as 128 blocks of 16, split into
+    sparse blocks of 8."""
+    rng = np.random.default_rng(seed)
+    rows = seqs * seq_len
+    cand = np.full((rows, k), -1, np.int32)
+    ks = np.repeat(np.arange(seqs, dtype=np.int64) * seq_len, seq_len).astype(np.int32)
+    ke = (ks + np.tile(np.arange(1, seq_len + 1), seqs)).astype(np.int32)
+    width = ratio * sparse_block
+    for r in range(rows):
+        avail = (int(ke[r] - ks[r]) + width - 1) // width
+        take = min(k, avail)
+        cand[r, :take] = rng.choice(avail, take, replace=False)
+    return SparseExpand(f"sparse_expand_{rows}x{k}", cand, ks, ke, ratio, sparse_block)
 
 
 def retarget(case: InsertCase, record: int, page_stride: Optional[int] = None) -> InsertCase:

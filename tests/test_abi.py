@@ -21,7 +21,7 @@ from quantized_paged_kv_rope_amd import build as KB
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvrec.h")
 
-OK, NULL, RECORD, BLOCK, STRIDE, ALIGN, SIZE, OPTION = 0, -1, -2, -3, -4, -5, -6, -8
+OK, NULL, RECORD, BLOCK, STRIDE, ALIGN, SIZE, OPTION, OVERLAP = 0, -1, -2, -3, -4, -5, -6, -8, -9
 FAKE = 0x10000  # aligned, never dereferenced
 
 
@@ -66,7 +66,7 @@ def test_library_does_not_depend_on_the_oracle():
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, RECORD, BLOCK, STRIDE, ALIGN, SIZE, -7, OPTION, 12345):
+    for code in (OK, NULL, RECORD, BLOCK, STRIDE, ALIGN, SIZE, -7, OPTION, OVERLAP, 12345):
         s = lib.kvrec_status_str(code)
         assert s and isinstance(s, bytes)
     assert lib.kvrec_status_str(OK) == b"ok"
@@ -232,6 +232,76 @@ def test_insert_full_validation(lib):
     assert ins_ex(lib, f8, None, rec=512) == RECORD
     assert gat(lib, bf) == RECORD
     assert gat(lib, f8) == RECORD
+
+
+def qkv(lib, c, q_in=FAKE * 64, q_out=FAKE * 64, heads=8, eps=1e-6, norm=1, n=8, kv=FAKE,
+        slots=FAKE, pos=FAKE, cs=FAKE, max_pos=16, bs=64, rec=528):
+    return lib.kvrec_qnorm_rope_insert(q_in, q_out, heads, eps, norm, kv, n,
+                                       ctypes.byref(c) if c is not None else None, slots, pos,
+                                       cs, max_pos, bs, rec, None)
+
+
+def test_qnorm_rope_insert_validation(lib):
+    good = cache()
+    assert qkv(lib, good, n=0) == OK
+    assert qkv(lib, good, n=0, q_in=None, q_out=None, kv=None, slots=None, pos=None,
+               cs=None) == OK
+    assert qkv(lib, None) == NULL
+    for arg in ("q_in", "q_out", "kv", "slots", "pos", "cs"):
+        assert qkv(lib, good, **{arg: None}) == NULL, arg
+    assert qkv(lib, good, rec=584) == RECORD
+    assert qkv(lib, cache(rec=1024, stride=65536), rec=1024) == RECORD  # packed only
+    assert qkv(lib, good, bs=32) == BLOCK
+    assert qkv(lib, good, heads=0) == SIZE
+    assert qkv(lib, good, heads=1025) == SIZE
+    assert qkv(lib, good, heads=1024, n=2 ** 20 + 1) == SIZE         # tokens * heads > 2^30
+    assert qkv(lib, good, heads=1024, n=-1) == SIZE
+    assert qkv(lib, good, norm=2) == OPTION
+    assert qkv(lib, good, eps=0.0) == OPTION
+    assert qkv(lib, good, eps=-1e-6) == OPTION
+    assert qkv(lib, good, eps=float("inf")) == OPTION
+    assert qkv(lib, good, eps=0.0, norm=0, n=0) == OK                # eps unused
+    assert qkv(lib, good, max_pos=0) == SIZE
+    assert qkv(lib, good, q_in=FAKE * 64 + 8) == ALIGN
+    assert qkv(lib, good, q_out=FAKE * 64 + 8) == ALIGN
+    # in place is fine; a partial overlap is not
+    row = 8 * 512 * 2  # one token's q rows
+    assert qkv(lib, good, q_out=FAKE * 64 + row, n=0) == OK
+    assert qkv(lib, good, q_out=FAKE * 64 + row) == OVERLAP
+    assert qkv(lib, good, q_out=FAKE * 64 - row) == OVERLAP
+
+
+def expand(lib, rows=4, k=64, ratio=2, sbk=8, cand=FAKE, cs=None, ks=FAKE, kss=1, ke=FAKE,
+           kes=1, out=FAKE, ss=None, end=FAKE, es=1):
+    cs = k if cs is None else cs
+    ss = k * ratio if ss is None else ss
+    return lib.kvrec_expand_candidates(cand, cs, ks, kss, ke, kes, rows, k, ratio, sbk, out, ss,
+                                       end, es, None)
+
+
+def test_expand_candidates_validation(lib):
+    assert expand(lib, rows=0) == OK
+    assert expand(lib, rows=0, cand=None, ks=None, ke=None, out=None, end=None) == OK
+    for arg in ("cand", "ks", "ke", "out", "end"):
+        assert expand(lib, **{arg: None}) == NULL, arg
+    for k in (0, 3, 48, 2048):
+        assert expand(lib, k=k, ratio=1) == SIZE, k
+    assert expand(lib, k=1024, ratio=2) == SIZE            # K * ratio > 1024
+    assert expand(lib, k=1024, ratio=1, rows=0) == OK
+    assert expand(lib, ratio=3) == OPTION
+    assert expand(lib, ratio=0) == OPTION
+    assert expand(lib, sbk=4) == OPTION
+    assert expand(lib, sbk=32) == OPTION
+    assert expand(lib, rows=-1) == SIZE
+    assert expand(lib, rows=2 ** 30 + 1) == SIZE
+    assert expand(lib, cs=63) == SIZE                      # row stride < K
+    assert expand(lib, ss=127) == SIZE                     # row stride < K * ratio
+    assert expand(lib, kss=0) == SIZE
+    assert expand(lib, kes=0) == SIZE
+    assert expand(lib, es=0) == SIZE
+    assert expand(lib, cand=FAKE + 2) == ALIGN
+    assert expand(lib, out=FAKE + 1) == ALIGN
+    assert expand(lib, end=FAKE + 2) == ALIGN
 
 
 def test_legacy_cache_accepted(lib):

@@ -128,3 +128,26 @@ def test_full_prefill_262144(record):
     assert np.array_equal(got, want), P.first_diff(got, want)
     del d
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("record", [W.RECORD_BF16, W.RECORD_LEGACY])
+def test_bf16_rounding_edges(record):
+    """Rotated values spanning fp32/bf16 subnormals up to 2^126 (the inputs
+    are log-uniform in magnitude), rounded to bf16 by the kernel's
+    conversion: the bf16 cache and the legacy record's bf16 tail."""
+    rng = np.random.default_rng(77 + record)
+    n, bs = 2000, 32
+    case = W.custom_insert(2024 + record, n, record, bs, n // bs + 8, max_pos=5000,
+                           drop_frac=0.0)
+    mag = 10.0 ** rng.uniform(-44.0, 37.0, (n, 512))
+    x = (rng.choice([-1.0, 1.0], (n, 512)) * mag).astype(np.float32)
+    case.kv_bits = W.to_bf16_bits(x)
+    d = P.DeviceCase(case)
+    if record == W.RECORD_BF16:
+        d.insert_full(None)
+        want = _oracle(case, None)
+    else:
+        d.insert()
+        want = P.oracle_insert(case, case.initial_backing())
+    got = d.backing_host()
+    assert np.array_equal(got, want), P.first_diff(got, want)

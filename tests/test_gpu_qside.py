@@ -1,0 +1,162 @@
+"""GPU parity of the attention write (kvrec_qnorm_rope_insert): the q side
+(per-head RMSNorm, then the NeoX rotation of the tail) fused with the KV
+insert in one launch.
+
+The cache bytes must equal the oracle's exactly. The q rows are compared
+with the oracle's correctly rounded binary64 result within the error bound
+of the kernel's fp32 arithmetic. With u = 2^-24: the squares and the sum of
+512 positive terms (7 sequential then 6 pairwise adds) carry at most 14u
+relative error, the + eps one more u, v_rsq_f32 at most 1 ulp (2u) plus half
+its input's error, and y = x * inv one more u: y is within 10.5u of exact.
+A rotated element y1*c - y2*s adds a rounding per product and one for the
+difference: within 12.5u * (|y1 c| + |y2 s|). Rounding both sides to bf16
+adds at most one bf16 ulp between them. So per element
+    |got - want| <= 2^-20 * m + ulp_bf16(max(|got|, |want|)),
+with m = |y| for dims 0..447 and |y1 c| + |y2 s| for the tail (from the
+exact values), and without the norm the same bound holds a fortiori.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_paged_kv_rope_amd import binding as B
+from quantized_paged_kv_rope_amd import workloads as W
+from tests import parity_util as P
+
+pytestmark = pytest.mark.gpu
+
+RNG = np.random.default_rng(6060)
+
+
+def _val(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _magnitude(q_bits, positions, table, eps, apply_norm):
+    """m of the bound: |y| (NoPE) and |y1 c| + |y2 s| (tail), in float64."""
+    x = _val(q_bits)
+    if apply_norm:
+        x = x / np.sqrt((x ** 2).mean(axis=2, keepdims=True) + eps)
+    cs = table[positions].astype(np.float64)[:, None, :]
+    c, s = np.abs(cs[..., :32]), np.abs(cs[..., 32:])
+    m = np.abs(x)
+    y1, y2 = m[..., 448:480].copy(), m[..., 480:].copy()
+    m[..., 448:480] = y1 * c + y2 * s
+    m[..., 480:] = y2 * c + y1 * s
+    return m
+
+
+def _check_q(got, want, m):
+    g, w = _val(got), _val(want)
+    big = np.maximum(np.abs(g), np.abs(w))
+    ulp = np.where(big > 0, 2.0 ** (np.floor(np.log2(np.maximum(big, 1e-300))) - 7), 0.0)
+    ulp = np.maximum(ulp, 2.0 ** -133)  # bf16 subnormal spacing
+    bad = np.abs(g - w) > 2.0 ** -20 * m + ulp
+    assert not bad.any(), (f"{bad.sum()} q elements outside the bound; first at "
+                           f"{np.argwhere(bad)[0]}: got {g[bad][0]!r}, want {w[bad][0]!r}")
+    return float((got == want).mean())
+
+
+def _run(aw, apply_norm=True, in_place=True, q_out_init=None):
+    case = aw.insert
+    d = P.DeviceCase(case)
+    q = P.dev_bf16(aw.q_bits.reshape(-1, 512)).view(aw.q_bits.shape)
+    out = q if in_place else P.dev_bf16(q_out_init.reshape(-1, 512)).view(aw.q_bits.shape)
+    B.kvrec_qnorm_rope_insert(q, d.kv, d.k_cache, d.slots, d.positions, d.cos_sin,
+                              case.block_size, eps=aw.eps, apply_q_norm=apply_norm,
+                              q_out=None if in_place else out)
+    got_q = P.host_bits(out.reshape(-1, 512)).reshape(aw.q_bits.shape)
+    got_cache = d.backing_host()
+    if not in_place:
+        assert np.array_equal(P.host_bits(q.reshape(-1, 512)).reshape(aw.q_bits.shape),
+                              aw.q_bits), "q_in was modified"
+    return got_q, got_cache
+
+
+def _small(seed, n, heads, record, max_pos=700):
+    case = W.custom_insert(seed, n, record, 16, (n * 5 // 4) // 16 + 2, max_pos=max_pos,
+                           scale_rows=True)
+    x = RNG.standard_normal((n, heads, 512)).astype(np.float32)
+    x *= RNG.uniform(0.01, 30.0, (n, heads, 1)).astype(np.float32)
+    if n > 2:
+        x[1, 0, :] = 0.0  # an all-zero head
+    return W.AttentionWrite(f"qside_{n}x{heads}", W.to_bf16_bits(x), 1e-6, case)
+
+
+def test_worked_heads(golden):
+    gq = golden["q_side"]
+    inp = gq["inputs"]
+    x = np.zeros((1, inp["heads"], 512), np.float32)
+    x[0, 0, :] = 2.0
+    x[0, 1, 0] = 16.0
+    table = np.zeros((inp["max_pos"], 64), np.float32)
+    table[:, :32] = 1.0
+    table[1, 0], table[1, 32] = 0.5, 0.75
+    case = W.InsertCase("qside_worked", 528, 4, 1, 2560, W.to_bf16_bits(np.ones((1, 512))),
+                        np.array([2], np.int64), np.array([inp["position"]], np.int64), table,
+                        backing_seed=5)
+    got_q, _ = _run(W.AttentionWrite("worked", W.to_bf16_bits(x), inp["eps"], case))
+    for h in (0, 1):
+        for dim, v in gq[f"head{h}"]["elements"].items():
+            assert int(got_q[0, h, int(dim)]) == v, (h, dim)
+
+
+@pytest.mark.parametrize("record", [528, 584])
+@pytest.mark.parametrize("apply_norm", [True, False])
+@pytest.mark.parametrize("n,heads", [(1, 1), (17, 3), (300, 16), (64, 128), (5, 1024)])
+def test_attention_write_small(record, apply_norm, n, heads):
+    aw = _small(9100 + n + heads + record, n, heads, record)
+    case = aw.insert
+    got_q, got_cache = _run(aw, apply_norm)
+    want_cache = P.oracle_insert(case, case.initial_backing())
+    assert np.array_equal(got_cache, want_cache), P.first_diff(got_cache, want_cache)
+    want_q = oracle.qnorm_rope(aw.q_bits, case.positions, case.cos_sin, aw.eps, apply_norm)
+    same = _check_q(got_q, want_q, _magnitude(aw.q_bits, case.positions, case.cos_sin, aw.eps,
+                                              apply_norm))
+    assert same > 0.99, same
+
+
+def test_out_of_place_and_out_of_range_positions():
+    aw = _small(321, 40, 8, 528)
+    case = aw.insert
+    case.positions = case.positions.copy()
+    case.positions[[3, 7]] = [-1, 700]  # out of range: rows unwritten, token not inserted
+    sentinel = np.full_like(aw.q_bits, 0x1234)
+    got_q, got_cache = _run(aw, in_place=False, q_out_init=sentinel)
+    assert (got_q[3] == 0x1234).all() and (got_q[7] == 0x1234).all()
+    want_q = oracle.qnorm_rope(aw.q_bits, case.positions, case.cos_sin, aw.eps,
+                               out=sentinel.copy())
+    _check_q(got_q, want_q, _magnitude(aw.q_bits, np.clip(case.positions, 0, 699),
+                                       case.cos_sin, aw.eps, True))
+    want_cache = P.oracle_insert(case, case.initial_backing())
+    assert np.array_equal(got_cache, want_cache), P.first_diff(got_cache, want_cache)
+
+
+def test_skipped_slots_still_process_q():
+    aw = _small(654, 32, 4, 528)
+    aw.insert.slot_mapping[:] = -1
+    got_q, got_cache = _run(aw)
+    assert np.array_equal(got_cache, aw.insert.initial_backing())
+    want_q = oracle.qnorm_rope(aw.q_bits, aw.insert.positions, aw.insert.cos_sin, aw.eps)
+    _check_q(got_q, want_q, _magnitude(aw.q_bits, aw.insert.positions, aw.insert.cos_sin,
+                                       aw.eps, True))
+
+
+def test_attention_write_4096x128():
+    """The benchmark's workload in its launch configuration: the cache bytes
+    in full, the q rows of 96 sampled tokens (all 128 heads each)."""
+    aw = W.attention_write()
+    case = aw.insert
+    got_q, got_cache = _run(aw)
+    want_cache = P.oracle_insert(case, case.initial_backing())
+    assert np.array_equal(got_cache, want_cache), P.first_diff(got_cache, want_cache)
+    toks = np.sort(RNG.choice(case.num_tokens, 96, replace=False))
+    toks[:2] = [0, case.num_tokens - 1]
+    want_q = oracle.qnorm_rope(aw.q_bits[toks], case.positions[toks], case.cos_sin, aw.eps)
+    same = _check_q(got_q[toks], want_q, _magnitude(aw.q_bits[toks], case.positions[toks],
+                                                    case.cos_sin, aw.eps, True))
+    assert same > 0.99, same
+    torch.cuda.empty_cache()
