@@ -480,8 +480,10 @@ int orc_gather(const uint8_t *cache, int64_t num_blocks, int64_t page_stride,
 /* (base when none is valid); and count the valid sparse token columns,     */
 /* end = (n_valid - 1) * SBK + min(max(ke - (last * SBK + ks), 1), SBK), or  */
 /* 0 when none is valid (only the last block can be partial). Readings: S = */
-/* K * RATIO (the store covers every expanded position); ks >= 0, so the     */
-/* page's integer division is plain; the int32 arithmetic does not wrap.     */
+/* K * RATIO (the store covers every expanded position); ks >= 0 and ke >= 0 */
+/* (so the page's integer division is plain); intermediate values (2c + 1,   */
+/* ke - ks + SBK - 1, last * SBK + ks) are exact integers, not wrapped to    */
+/* int32 (every stored result fits in int32).                                */
 /* ------------------------------------------------------------------------ */
 static int compare_int32(const void *a, const void *b) {
   int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
@@ -496,9 +498,10 @@ int orc_expand_candidates(const int32_t *cand, int64_t cand_stride, const int32_
   int64_t r;
   int32_t i, j;
   int32_t L = num_candidates * ratio;
-  int32_t *blocks, *kept;
+  int64_t *blocks;
+  int32_t *kept;
   if (num_candidates < 1 || (ratio != 1 && ratio != 2) || sparse_block < 1) return -1;
-  blocks = (int32_t *)malloc(sizeof(int32_t) * (size_t)L);
+  blocks = (int64_t *)malloc(sizeof(int64_t) * (size_t)L);
   kept = (int32_t *)malloc(sizeof(int32_t) * (size_t)L);
   if (blocks == NULL || kept == NULL) {
     free(blocks);
@@ -507,17 +510,18 @@ int orc_expand_candidates(const int32_t *cand, int64_t cand_stride, const int32_
   }
   for (r = 0; r < rows; ++r) {
     const int32_t *c = cand + r * cand_stride;
-    int32_t ks = row_ks[r * ks_stride], ke = row_ke[r * ke_stride];
-    int32_t kv_len = ke - ks > 0 ? ke - ks : 0;
-    int32_t max_block = (kv_len + sparse_block - 1) / sparse_block;
-    int32_t base = ks / sparse_block;
-    int32_t n_valid = 0, last = -1, pad, fill, last_start;
+    int64_t ks = row_ks[r * ks_stride], ke = row_ke[r * ke_stride];
+    int64_t kv_len = ke - ks > 0 ? ke - ks : 0;
+    int64_t max_block = (kv_len + sparse_block - 1) / sparse_block;
+    int64_t base = ks / sparse_block;
+    int64_t last = -1, fill, last_start;
+    int32_t n_valid = 0, pad;
     int32_t *out = sparse + r * sparse_stride;
     /* expand */
     for (i = 0; i < num_candidates; ++i) {
       if (ratio == 2) {
-        blocks[2 * i] = c[i] * 2;
-        blocks[2 * i + 1] = c[i] * 2 + 1;
+        blocks[2 * i] = (int64_t)c[i] * 2;
+        blocks[2 * i + 1] = (int64_t)c[i] * 2 + 1;
       } else {
         blocks[i] = c[i];
       }
@@ -525,18 +529,18 @@ int orc_expand_candidates(const int32_t *cand, int64_t cand_stride, const int32_
     /* filter */
     for (i = 0; i < L; ++i)
       if (blocks[i] >= 0 && blocks[i] < max_block) {
-        kept[n_valid++] = blocks[i];
+        kept[n_valid++] = (int32_t)blocks[i];
         if (blocks[i] > last) last = blocks[i];
       }
     /* sort ascending */
     qsort(kept, (size_t)n_valid, sizeof(int32_t), compare_int32);
     /* emit and pad */
-    pad = n_valid > 0 ? last + base : base;
-    for (j = 0; j < L; ++j) out[j] = j < n_valid ? kept[j] + base : pad;
+    pad = (int32_t)(n_valid > 0 ? last + base : base);
+    for (j = 0; j < L; ++j) out[j] = j < n_valid ? (int32_t)(kept[j] + base) : pad;
     last_start = last * sparse_block + ks;
     fill = ke - last_start > 1 ? ke - last_start : 1;
     if (fill > sparse_block) fill = sparse_block;
-    end[r * end_stride] = n_valid > 0 ? (n_valid - 1) * sparse_block + fill : 0;
+    end[r * end_stride] = n_valid > 0 ? (int32_t)((n_valid - 1) * (int64_t)sparse_block + fill) : 0;
   }
   free(blocks);
   free(kept);
