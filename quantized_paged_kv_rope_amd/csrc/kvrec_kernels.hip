@@ -51,11 +51,11 @@ constexpr int kWave = 64;
 constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kHalfRowMirror = 0x141;  // lane i <-> 7-i within 8 lanes
+// ds_swizzle bit-mask mode: and 0x1F, or 0, xor 4 -> partner lane l ^ 4.
+constexpr int kSwizzleXor4 = 0x1F | (4 << 10);
 constexpr int kRowShl4 = 0x104;        // lane i reads lane i+4 of its 16-lane row
 constexpr int kRowShl8 = 0x108;
 constexpr int kRowShl12 = 0x10C;
-// ds_swizzle bit-mask mode: and 0x1F, or 0, xor 4 -> partner lane l ^ 4.
-constexpr int kSwizzleXor4 = 0x1F | (4 << 10);
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -164,6 +164,8 @@ __device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
   return max(v, dpp<Ctrl>(v));
 }
 
+
+
 __device__ __forceinline__ uint32_t lane_read(uint32_t v, int src_lane) {
   return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src_lane << 2, static_cast<int>(v)));
 }
@@ -235,6 +237,9 @@ template <bool kScaled = false>
 __device__ __forceinline__ void rope_tail(float f[8], const u32x4 raw, int lane, const f32x4 c0,
                                           const f32x4 c1, const f32x4 s0, const f32x4 s1,
                                           float inv = 1.0f) {
+  // Partner lane l ^ 4 by ds_swizzle (bit-mask mode, no VALU issue: two DPP
+  // moves per dword would add 8 VALU instructions, which the fp8 cache's
+  // division-heavy insert measurably pays for).
   u32x4 pr;
   pr.x = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(raw.x), kSwizzleXor4));
   pr.y = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(raw.y), kSwizzleXor4));
@@ -421,17 +426,12 @@ __device__ __forceinline__ void load_table(const f32x4 *cos_sin, uint32_t row, i
 // saves each wave a dependent kernarg load before its first memory request.
 // kOptions = false is the plain insert (NeoX, ratio 1, no floor, positions
 // present); its code carries none of the option checks below.
-// One wave's share of the insert: tokens t0 .. t0+T-1 (t0 < n).
+// One wave's share of the insert: tokens t0 .. t0+T-1 (t0 < n), ratio 1
+// (the compressed-KV gate runs in insert_group_kernel).
 template <int P, int T, int kFmt, int kRope, bool kSanitize, bool kOptions>
 __device__ __forceinline__ void insert_wave(const InsertArgs &a, uint32_t t0, int lane,
-                                            uint32_t ratio, uint32_t ratio_magic,
-                                            uint32_t ratio_shift, uint32_t amax_floor_bits,
-                                            float scale) {
-  // With a compression ratio above 1 most tokens are gated off, so the kv
-  // row is read only once the gate has passed; otherwise it is read at once,
-  // beside the slot and position.
-  const bool defer = kOptions && ratio > 1;
-  // No positions: only the rotation-free insert with ratio 1 (host-checked).
+                                            uint32_t amax_floor_bits, const float *fp8_scale) {
+  // No positions: only the rotation-free insert (host-checked).
   const bool has_pos = !kOptions || a.positions != nullptr;
   u32x4 raw[T];
   int64_t sl[T], ps[T];
@@ -439,14 +439,23 @@ __device__ __forceinline__ void insert_wave(const InsertArgs &a, uint32_t t0, in
   for (int k = 0; k < T; ++k) {
     const uint32_t t = t0 + k;
     const bool in = (T == 1) || t < a.n;
-    raw[k] = in && !defer
-                 ? ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t) * kWave + lane)
-                 : u32x4{0, 0, 0, 0};
+    raw[k] = in ? ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t) * kWave + lane)
+                : u32x4{0, 0, 0, 0};
     sl[k] = in ? a.slots[t] : -1;
     ps[k] = !has_pos ? 0 : in ? a.positions[t] : -1;
   }
   // All three loads are issued before anything waits on the slot or position.
   __builtin_amdgcn_sched_barrier(0);
+  // The page geometry comes in kernel arguments past the ones gfx950 preloads
+  // into SGPRs. Reading them here issues their loads beside the slot and
+  // position loads, so they arrive with the same wait instead of costing a
+  // round trip just before the store.
+  asm volatile("" ::"s"(a.block_size), "s"(a.div_magic), "s"(a.div_shift), "s"(a.page_stride),
+               "s"(a.base));
+  // The fp8 cache's per-tensor scale (one uniform load per wave) is needed
+  // only at the encode: it is read after the token's loads are in flight.
+  float scale = 1.0f;
+  if constexpr (kFmt == kFmtFp8) scale = *fp8_scale;
   uint32_t slot[T], row[T];
   bool ok[T];
 #pragma unroll
@@ -454,17 +463,6 @@ __device__ __forceinline__ void insert_wave(const InsertArgs &a, uint32_t t0, in
     ok[k] = below(sl[k], a.total_slots) && (!has_pos || below(ps[k], a.max_pos));
     slot[k] = static_cast<uint32_t>(sl[k]);
     row[k] = static_cast<uint32_t>(ps[k]);
-    if (kOptions && ratio > 1) {
-      // Compressed-KV gate ([MXFP8 record] 关键源码片段): write only when
-      // (pos + 1) % ratio == 0, rotating with row pos / ratio * ratio, which
-      // is then pos + 1 - ratio. pos + 1 <= 2^30, so the division is exact.
-      const uint32_t p1 = row[k] + 1;
-      const uint32_t q = (__umulhi(p1, ratio_magic) + p1) >> ratio_shift;
-      ok[k] = ok[k] && p1 == q * ratio;
-      row[k] = p1 - ratio;
-      if (ok[k])
-        raw[k] = ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t0 + k) * kWave + lane);
-    }
   }
   // The kv row is used only on the encode path; left to itself the compiler
   // sinks its load there, behind the wait for the slot and position. An
@@ -472,7 +470,7 @@ __device__ __forceinline__ void insert_wave(const InsertArgs &a, uint32_t t0, in
   // flight together with the slot and position loads.
 #pragma unroll
   for (int k = 0; k < T; ++k)
-    if (!defer && !ok[k]) asm volatile("" ::"v"(raw[k]));
+    if (!ok[k]) asm volatile("" ::"v"(raw[k]));
   // Only lanes 56..63 read (and later use) the cos/sin values. The empty asm
   // statements give the registers an unset value in the other lanes, so the
   // compiler does not spend moves per token zero-filling them.
@@ -494,19 +492,14 @@ __global__ __launch_bounds__(W * kWave) void insert_kernel(
     uint32_t n, uint32_t per_xcd, const u32x4 *kv, const int64_t *slots, const int64_t *positions,
     const f32x4 *cos_sin, uint32_t max_pos, uint32_t total_slots, uint8_t *base,
     int64_t page_stride, uint32_t block_size, uint32_t div_magic, uint32_t div_shift,
-    uint32_t ratio, uint32_t ratio_magic, uint32_t ratio_shift, uint32_t amax_floor_bits,
-    const float *fp8_scale) {
+    uint32_t amax_floor_bits, const float *fp8_scale) {
   const InsertArgs a{kv,         slots,       positions, cos_sin,   base,    page_stride, n,
                      block_size, total_slots, div_magic, div_shift, max_pos};
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t t0 = (xcd_block(per_xcd) * W + wave) * T;
   if (t0 >= a.n) return;
-  // The per-tensor scale of the fp8 cache: one uniform load per wave.
-  float scale = 1.0f;
-  if constexpr (kFmt == kFmtFp8) scale = *fp8_scale;
-  insert_wave<P, T, kFmt, kRope, kSanitize, kOptions>(a, t0, lane, ratio, ratio_magic,
-                                                      ratio_shift, amax_floor_bits, scale);
+  insert_wave<P, T, kFmt, kRope, kSanitize, kOptions>(a, t0, lane, amax_floor_bits, fp8_scale);
 }
 
 // Sum of a value over the 64 lanes, returned in every lane. Each step adds a
@@ -538,6 +531,9 @@ template <int P, int HPW, bool kNorm>
 __device__ __forceinline__ void qnorm_rope_wave(const InsertArgs &a, const u32x4 *q_in,
                                                 u32x4 *q_out, uint32_t t, uint32_t h0,
                                                 uint32_t heads, int lane, float eps) {
+  // The position (and then the table row, which needs it) is requested
+  // before the q rows: measured on MI355X, issuing the 2 KB of q rows first
+  // delayed the table row behind them (193 against 180 us at 4096 x 128).
   const int64_t ps = a.positions[t];
   if (!below(ps, a.max_pos)) return;
   f32x4 c0, c1, s0, s1;
@@ -576,14 +572,15 @@ __device__ __forceinline__ void qnorm_rope_wave(const InsertArgs &a, const u32x4
 // The attention write: the q side for every (token, head group) and the KV
 // insert for every token, in one launch. Waves [0, q_waves) take head group
 // w % wpt of token w / wpt; waves [q_waves, q_waves + n) take one token's
-// insert each.
+// insert each. The arguments a q wave needs come first: they fill exactly the
+// 16 dwords gfx950 preloads into SGPRs.
 template <int P, int kFmt, int HPW, bool kNorm>
 __global__ __launch_bounds__(kWave) void qkv_kernel(
-    uint32_t n, uint32_t per_xcd, const u32x4 *kv, const int64_t *slots, const int64_t *positions,
-    const f32x4 *cos_sin, uint32_t max_pos, uint32_t total_slots, uint8_t *base,
-    int64_t page_stride, uint32_t block_size, uint32_t div_magic, uint32_t div_shift,
-    const u32x4 *q_in, u32x4 *q_out, uint32_t heads, uint32_t q_waves, uint32_t wpt,
-    uint32_t wpt_magic, uint32_t wpt_shift, float eps) {
+    uint32_t per_xcd, uint32_t q_waves, uint32_t wpt, uint32_t wpt_magic, uint32_t wpt_shift,
+    uint32_t heads, float eps, uint32_t max_pos, const u32x4 *q_in, u32x4 *q_out,
+    const int64_t *positions, const f32x4 *cos_sin, uint32_t n, const u32x4 *kv,
+    const int64_t *slots, uint32_t total_slots, uint8_t *base, int64_t page_stride,
+    uint32_t block_size, uint32_t div_magic, uint32_t div_shift) {
   const InsertArgs a{kv,         slots,       positions, cos_sin,   base,    page_stride, n,
                      block_size, total_slots, div_magic, div_shift, max_pos};
   const int lane = threadIdx.x;
@@ -595,43 +592,50 @@ __global__ __launch_bounds__(kWave) void qkv_kernel(
   }
   const uint32_t t0 = w - q_waves;
   if (t0 >= a.n) return;
-  insert_wave<P, 1, kFmt, kRopeNeox, false, false>(a, t0, lane, 1, 0, 0, 0, 1.0f);
+  insert_wave<P, 1, kFmt, kRopeNeox, false, false>(a, t0, lane, 0, nullptr);
 }
 
-// The compressed-KV insert with a ratio R > 1 ([MXFP8 record] 关键源码片段)
-// writes one token in R. One wave per token would spend most waves on a
-// slot/position round trip and nothing else, so here each wave takes a
-// group of `group` (<= 64) consecutive tokens: lane j reads the slot and
-// position of token j of the group and evaluates the gate, a ballot collects
-// the kept tokens, and the wave then encodes only those, two at a time so
-// that their kv and table loads are in flight together (a group holds about
-// two kept tokens, see gated_group). The work per kept
-// token (and every byte written) is that of insert_kernel.
-template <int P, int kFmt, int kRope, bool kSanitize>
-__global__ __launch_bounds__(kWave) void insert_gated_kernel(
+// Grouped insert: each wave takes a group of `group` (<= 64) consecutive
+// tokens. Lane j reads the slot and position of token j of the group in one
+// vector load (and, for the compressed-KV insert with a ratio R > 1 of
+// [MXFP8 record] 关键源码片段, evaluates the gate); a ballot collects the
+// tokens to write, and the wave encodes them two at a time so that their kv
+// and table loads are in flight together. Against one wave per token this
+// replaces the per-token scalar slot/position round trip (the table row waits
+// on it) by one vector load per group, and lets a gated-off token cost only
+// its slot and position. The work per written token (and every byte written)
+// is that of insert_kernel.
+template <int P, int kFmt, int kRope, bool kSanitize, bool kOptions, bool kGate>
+__global__ __launch_bounds__(kWave) void insert_group_kernel(
     uint32_t n, uint32_t per_xcd, const u32x4 *kv, const int64_t *slots, const int64_t *positions,
     const f32x4 *cos_sin, uint32_t max_pos, uint32_t total_slots, uint8_t *base,
     int64_t page_stride, uint32_t block_size, uint32_t div_magic, uint32_t div_shift,
     uint32_t ratio, uint32_t ratio_magic, uint32_t ratio_shift, uint32_t amax_floor_bits,
-    uint32_t group) {
+    uint32_t group, const float *fp8_scale) {
   const InsertArgs a{kv,         slots,       positions, cos_sin,   base,    page_stride, n,
                      block_size, total_slots, div_magic, div_shift, max_pos};
   const int lane = threadIdx.x;
   const uint32_t t0 = xcd_block(per_xcd) * group;
   if (t0 >= a.n) return;
+  float scale = 1.0f;
+  if constexpr (kFmt == kFmtFp8) scale = *fp8_scale;
 
   bool ok = false;
   uint32_t slot = 0, row = 0;
   if (static_cast<uint32_t>(lane) < group && t0 + lane < a.n) {
     const int64_t sl = ld<(P & kNtKv) != 0>(a.slots + t0 + lane);
     const int64_t ps = ld<(P & kNtKv) != 0>(a.positions + t0 + lane);
-    // (pos + 1) % R == 0, rotating with row pos / R * R = pos + 1 - R;
-    // pos + 1 <= 2^30, so the magic-number division is exact.
-    const uint32_t p1 = static_cast<uint32_t>(ps) + 1;
-    const uint32_t q = (__umulhi(p1, ratio_magic) + p1) >> ratio_shift;
-    ok = below(sl, a.total_slots) && below(ps, a.max_pos) && p1 == q * ratio;
+    ok = below(sl, a.total_slots) && below(ps, a.max_pos);
     slot = static_cast<uint32_t>(sl);
-    row = p1 - ratio;
+    row = static_cast<uint32_t>(ps);
+    if constexpr (kGate) {
+      // (pos + 1) % R == 0, rotating with row pos / R * R = pos + 1 - R;
+      // pos + 1 <= 2^30, so the magic-number division is exact.
+      const uint32_t p1 = row + 1;
+      const uint32_t q = (__umulhi(p1, ratio_magic) + p1) >> ratio_shift;
+      ok = ok && p1 == q * ratio;
+      row = p1 - ratio;
+    }
   }
   uint64_t kept = __ballot(ok);
   while (kept != 0) {
@@ -652,11 +656,11 @@ __global__ __launch_bounds__(kWave) void insert_gated_kernel(
     asm("" : "=v"(d0), "=v"(d1), "=v"(e0), "=v"(e1));
     load_table<P, kRope>(a.cos_sin, row0, lane, c0, c1, s0, s1);
     load_table<P, kRope>(a.cos_sin, row1, lane, d0, d1, e0, e1);
-    encode_store<P, kFmt, kRope, kSanitize, true>(a, lane, raw0, c0, c1, s0, s1, slot0,
-                                                  amax_floor_bits, 1.0f);
+    encode_store<P, kFmt, kRope, kSanitize, kOptions>(a, lane, raw0, c0, c1, s0, s1, slot0,
+                                                      amax_floor_bits, scale);
     if (two)
-      encode_store<P, kFmt, kRope, kSanitize, true>(a, lane, raw1, d0, d1, e0, e1, slot1,
-                                                    amax_floor_bits, 1.0f);
+      encode_store<P, kFmt, kRope, kSanitize, kOptions>(a, lane, raw1, d0, d1, e0, e1, slot1,
+                                                        amax_floor_bits, scale);
   }
 }
 
@@ -780,29 +784,27 @@ hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const in
   uint8_t *base = g.base;
   int64_t stride = g.page_stride;
   uint32_t total = g.total_slots, bs = g.block_size, magic = g.div_magic, shift = g.div_shift;
-  uint32_t ratio = o.ratio, rmagic = o.ratio_magic, rshift = o.ratio_shift;
   uint32_t floor_bits = o.amax_floor_bits;
-  void *params[] = {&n32,  &per_xcd, &kv4,  &slots, &positions, &cs4,   &mp,
-                    &total, &base,    &stride, &bs,   &magic,     &shift, &ratio,
-                    &rmagic, &rshift, &floor_bits, &fp8_scale};
+  void *params[] = {&n32,  &per_xcd, &kv4,  &slots, &positions, &cs4,       &mp,
+                    &total, &base,    &stride, &bs,   &magic,     &shift,     &floor_bits,
+                    &fp8_scale};
   return hipLaunchKernel(
       reinterpret_cast<const void *>(insert_kernel<P, W, T, kFmt, kRope, kSanitize, kOptions>),
       grid,
       dim3(W * kWave), params, 0, stream);
 }
 
-// Tokens per wave of the gated kernel: about two kept tokens per group, i.e.
-// one round of loads per wave (measured on MI355X at the 262144-token prefill
-// shape: groups of R, 2R, 4R and 8R tokens took 33.6, 26.5, 27.8 and 30.0 us
-// at R = 4).
+// Tokens per wave of the gated insert (ratio R > 1): about two kept tokens
+// per group, i.e. one round of loads per wave (measured on MI355X at the
+// 262144-token prefill shape: groups of R, 2R, 4R and 8R tokens took 33.6,
+// 26.5, 27.8 and 30.0 us at R = 4).
 uint32_t gated_group(uint32_t ratio) { return ratio >= 32 ? 64u : 2u * ratio; }
 
-template <int kFmt, int kRope, bool kSanitize>
-hipError_t launch_insert_gated(const void *kv, int64_t n, const CacheGeom &g,
+template <int kFmt, int kRope, bool kSanitize, bool kOptions, bool kGate>
+hipError_t launch_insert_group(const void *kv, int64_t n, const CacheGeom &g,
                                const int64_t *slots, const int64_t *positions,
                                const float *cos_sin, int64_t max_pos, const InsertOptions &o,
-                               hipStream_t stream) {
-  uint32_t group = gated_group(o.ratio);
+                               uint32_t group, const float *fp8_scale, hipStream_t stream) {
   uint32_t per_xcd = 0;
   const dim3 grid = xcd_grid<1>((n + group - 1) / group, &per_xcd);
   uint32_t n32 = static_cast<uint32_t>(n), mp = static_cast<uint32_t>(max_pos);
@@ -815,9 +817,10 @@ hipError_t launch_insert_gated(const void *kv, int64_t n, const CacheGeom &g,
   uint32_t floor_bits = o.amax_floor_bits;
   void *params[] = {&n32,  &per_xcd, &kv4,  &slots, &positions, &cs4,   &mp,
                     &total, &base,    &stride, &bs,   &magic,     &shift, &ratio,
-                    &rmagic, &rshift, &floor_bits, &group};
+                    &rmagic, &rshift, &floor_bits, &group, &fp8_scale};
   return hipLaunchKernel(
-      reinterpret_cast<const void *>(insert_gated_kernel<kInsertPolicy, kFmt, kRope, kSanitize>),
+      reinterpret_cast<const void *>(
+          insert_group_kernel<kInsertPolicy, kFmt, kRope, kSanitize, kOptions, kGate>),
       grid, dim3(kWave), params, 0, stream);
 }
 
@@ -866,9 +869,9 @@ hipError_t launch_qkv_t(const QArgs &q, const void *kv, int64_t n, const CacheGe
   uint32_t wmagic = 0, wshift = 0;
   division_magic32(wpt, &wmagic, &wshift);
   float eps = q.eps;
-  void *params[] = {&n32,  &per_xcd, &kv4,   &slots, &positions, &cs4, &mp,      &total,
-                    &base, &stride,  &bs,    &magic, &shift,     &qi,  &qo,      &heads,
-                    &q_waves, &wpt,  &wmagic, &wshift, &eps};
+  void *params[] = {&per_xcd, &q_waves, &wpt,  &wmagic, &wshift, &heads, &eps,
+                    &mp,      &qi,      &qo,   &positions, &cs4,  &n32,  &kv4,
+                    &slots,   &total,   &base, &stride,    &bs,   &magic, &shift};
   return hipLaunchKernel(
       reinterpret_cast<const void *>(qkv_kernel<kInsertPolicy, kFmt, kQHeadsPerWave, kNorm>),
       grid, dim3(kWave), params, 0, stream);
@@ -910,13 +913,19 @@ hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const in
 #undef KVREC_PLAIN
   if (format != Format::kMxfp8 && format != Format::kLegacy) return hipErrorInvalidValue;
   const bool legacy = format == Format::kLegacy;
+  // Ratio R > 1: the gated group kernel. Ratio 1: one wave per token, as
+  // for the plain insert (measured on MI355X at 262144 tokens, groups of 2 or
+  // 4 tokens took 89-91 us for NeoX + sanitise against 81 us per token, and
+  // won under 2 us for the interleaved rotation).
 #define KVREC_INSERT(L, R, S)                                                                   \
-  if (legacy == (L == kFmtLegacy) && o.rope == R && o.sanitize == S)                            \
-    return o.ratio > 1                                                                          \
-               ? launch_insert_gated<L, R, S>(kv, n, g, slots, positions, cos_sin, max_pos, o,  \
-                                              stream)                                           \
-               : launch_insert_tuned<L, R, S>(kv, n, g, slots, positions, cos_sin, max_pos, o,  \
-                                              nullptr, stream);
+  if (legacy == (L == kFmtLegacy) && o.rope == R && o.sanitize == S) {                          \
+    if (o.ratio > 1)                                                                            \
+      return launch_insert_group<L, R, S, true, true>(kv, n, g, slots, positions, cos_sin,      \
+                                                      max_pos, o, gated_group(o.ratio),         \
+                                                      nullptr, stream);                         \
+    return launch_insert_tuned<L, R, S>(kv, n, g, slots, positions, cos_sin, max_pos, o,        \
+                                        nullptr, stream);                                       \
+  }
 #define KVREC_INSERT_R(L, R) KVREC_INSERT(L, R, false) KVREC_INSERT(L, R, true)
 #define KVREC_INSERT_L(L) \
   KVREC_INSERT_R(L, kRopeNeox) KVREC_INSERT_R(L, kRopeInterleaved) KVREC_INSERT_R(L, kRopeNone)

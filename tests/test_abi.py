@@ -354,5 +354,8 @@ def test_kernels_have_no_fma_and_no_packed_fp32():
     # fp32 denormals preserved for every kernel (mode 3 = keep inputs and outputs)
     modes = re.findall(r"\.amdhsa_float_denorm_mode_32\s+(\d+)", asm)
     assert modes and set(modes) == {"3"}
-    for needed in ("v_cvt_scalef32_pk_fp8_f32", "v_cvt_scalef32_pk_bf16_fp8", "ds_swizzle_b32"):
+    # the gfx950 scaled conversions, the bf16 conversion, and the NeoX partner
+    # exchange (ds_swizzle xor 4)
+    for needed in ("v_cvt_scalef32_pk_fp8_f32", "v_cvt_scalef32_pk_bf16_fp8", "v_cvt_pk_bf16_f32",
+                   "ds_swizzle_b32"):
         assert needed in code, needed
