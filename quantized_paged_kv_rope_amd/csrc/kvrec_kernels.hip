@@ -737,13 +737,22 @@ __global__ __launch_bounds__(W * kWave) void gather_kernel(
 // Launch configuration, chosen by timing every combination on MI355X, both as
 // single launches after the caches were cleaned and as the back-to-back
 // insert -> gather step (prefill 262144, legacy 65536, decode 16384 and a
-// 131072-row top-k gather). The insert's streamed inputs (kv rows, cos/sin
-// rows) are non-temporal while its records are stored normally: they are read
-// back soon, and the partial lines of scattered slots merge in cache. The
+// 131072-row top-k gather). The insert's kv rows are non-temporal (touched
+// once) while its records are stored normally: they are read back soon, and
+// the partial lines of scattered slots merge in cache; the cos/sin rows are
+// cached except for the bf16 cache (insert_policy below). The
 // gather's bf16 output is non-temporal: written once, and as large as the
 // Infinity Cache, it would otherwise evict the records. One wave per insert
 // block; two rows per gather wave, two waves per block.
-constexpr int kInsertPolicy = kNtKv | kNtTable;
+// Cache policy of the insert per format (measured on MI355X, back to back at
+// 262144 tokens): the kv rows non-temporal and the cos/sin rows cached took
+// the MXFP8 insert from 84.7 to 80.5 us (legacy 84 -> 80, fp8 102 -> 98, the
+// gated ratio-4 insert 26.4 -> 24.4); the bf16 cache, which writes 1 KB per
+// token, keeps its cos/sin loads non-temporal (91.5 us against 103).
+template <int kFmt>
+constexpr int insert_policy() {
+  return kFmt == kFmtBf16 ? (kNtKv | kNtTable) : kNtKv;
+}
 constexpr int kInsertWaves = 1;   // waves per block
 constexpr int kInsertTokens = 1;  // tokens per wave
 constexpr int kGatherPolicy = kNtOut;
@@ -820,7 +829,7 @@ hipError_t launch_insert_group(const void *kv, int64_t n, const CacheGeom &g,
                     &rmagic, &rshift, &floor_bits, &group, &fp8_scale};
   return hipLaunchKernel(
       reinterpret_cast<const void *>(
-          insert_group_kernel<kInsertPolicy, kFmt, kRope, kSanitize, kOptions, kGate>),
+          insert_group_kernel<insert_policy<kFmt>(), kFmt, kRope, kSanitize, kOptions, kGate>),
       grid, dim3(kWave), params, 0, stream);
 }
 
@@ -829,7 +838,7 @@ hipError_t launch_insert_tuned(const void *kv, int64_t n, const CacheGeom &g,
                                const int64_t *slots, const int64_t *positions,
                                const float *cos_sin, int64_t max_pos, const InsertOptions &o,
                                const float *fp8_scale, hipStream_t stream) {
-  return launch_insert<kInsertPolicy, kInsertWaves, kInsertTokens, kFmt, kRope, kSanitize,
+  return launch_insert<insert_policy<kFmt>(), kInsertWaves, kInsertTokens, kFmt, kRope, kSanitize,
                        kOptions>(kv, n, g, slots, positions, cos_sin, max_pos, o, fp8_scale,
                                  stream);
 }
@@ -873,7 +882,8 @@ hipError_t launch_qkv_t(const QArgs &q, const void *kv, int64_t n, const CacheGe
                     &mp,      &qi,      &qo,   &positions, &cs4,  &n32,  &kv4,
                     &slots,   &total,   &base, &stride,    &bs,   &magic, &shift};
   return hipLaunchKernel(
-      reinterpret_cast<const void *>(qkv_kernel<kInsertPolicy, kFmt, kQHeadsPerWave, kNorm>),
+      reinterpret_cast<const void *>(
+          qkv_kernel<insert_policy<kFmt>(), kFmt, kQHeadsPerWave, kNorm>),
       grid, dim3(kWave), params, 0, stream);
 }
 
