@@ -12,10 +12,12 @@
 // registers, E = max(L, 64) / 64 per lane (lane l holds positions
 // l*E .. l*E + E-1); positions past L and dropped blocks hold a sentinel
 // larger than any kept block. A bitonic network sorts the 64*E keys:
-// exchanges at distance < E stay inside a lane, the others go through
-// __shfl_xor (ds_bpermute) with lane distance j / E. The kept blocks then
-// occupy positions 0 .. n_valid-1 in order, and each lane writes its E
-// outputs.
+// exchanges at distance < E stay inside a lane; the others read the partner
+// lane by DPP (lane distances 1..8), ds_swizzle (16) or ds_bpermute (32), and
+// keep the smaller or larger key by one compare and one select, the direction
+// being a per-stage property of the lane. The kept count comes from ballots;
+// the kept blocks then occupy positions 0 .. n_valid-1 in order, and each
+// lane writes its E outputs.
 #include "kvrec_launch.h"
 
 namespace kvrec {
@@ -24,16 +26,91 @@ namespace {
 constexpr int kWave = 64;
 constexpr int32_t kSentinel = 0x7FFFFFFF;  // sorts after every kept block
 
-__device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m);
-  return v;
+// DPP controls (gfx9 encoding) and the ds_swizzle bit-mask pattern for xor 16.
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]: lane l ^ 1
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]: lane l ^ 2
+constexpr int kQuadReverse = 0x1B;   // quad_perm [3,2,1,0]: lane l ^ 3
+constexpr int kHalfRowMirror = 0x141;  // lane l ^ 7 within 8 lanes
+constexpr int kRowMirror = 0x140;      // lane l ^ 15 within 16 lanes
+constexpr int kSwizzleXor16 = 0x1F | (16 << 10);
+
+template <int Ctrl>
+__device__ __forceinline__ int32_t dpp(int32_t v) {
+  return __builtin_amdgcn_mov_dpp(v, Ctrl, 0xF, 0xF, true);
 }
 
-__device__ __forceinline__ int32_t wave_max_i32(int32_t v) {
+// The value held by lane l ^ D. Distances 1..8 are DPP moves (VALU, no LDS
+// round trip): xor 4 = (xor 7) then (xor 3), xor 8 = (xor 15) then (xor 7);
+// 16 is a ds_swizzle within 32 lanes, 32 a ds_bpermute.
+template <int D>
+__device__ __forceinline__ int32_t lane_xor(int32_t v, int32_t addr_xor32) {
+  if constexpr (D == 1) return dpp<kQuadXor1>(v);
+  else if constexpr (D == 2) return dpp<kQuadXor2>(v);
+  else if constexpr (D == 4) return dpp<kQuadReverse>(dpp<kHalfRowMirror>(v));
+  else if constexpr (D == 8) return dpp<kHalfRowMirror>(dpp<kRowMirror>(v));
+  else if constexpr (D == 16) return __builtin_amdgcn_ds_swizzle(v, kSwizzleXor16);
+  else return __builtin_amdgcn_ds_bpermute(addr_xor32, v);
+}
+
+// One stage of the bitonic network at distance J within runs of K keys, for
+// keys at positions i = lane * E + e. Position i keeps the smaller key of its
+// pair (i, i ^ J) when it is the pair's first and the run ascends
+// ((i & K) == 0), or when it is the second and the run descends; otherwise
+// the larger.
+template <int E, int K, int J>
+__device__ __forceinline__ void bitonic_stage(int32_t (&a)[E], int lane, int32_t addr_xor32) {
+  if constexpr (J < E) {
 #pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v = max(v, __shfl_xor(v, m));
-  return v;
+    for (int e = 0; e < E; ++e) {
+      constexpr int dummy = 0;
+      (void)dummy;
+      const int p = e ^ J;
+      if (p > e) {
+        if constexpr (K < E) {
+          // direction fixed by e alone
+          const int32_t lo = min(a[e], a[p]), hi = max(a[e], a[p]);
+          if ((e & K) == 0) {
+            a[e] = lo;
+            a[p] = hi;
+          } else {
+            a[e] = hi;
+            a[p] = lo;
+          }
+        } else {
+          // direction from the lane: ascending when ((lane * E) & K) == 0
+          const bool up = ((lane * E) & K) == 0;
+          const bool swap = (a[e] > a[p]) == up;
+          const int32_t x = a[e], y = a[p];
+          a[e] = swap ? y : x;
+          a[p] = swap ? x : y;
+        }
+      }
+    }
+  } else {
+    // partner in lane l ^ (J / E); keep the larger key when exactly one of
+    // "run descends" and "second of the pair" holds.
+    const bool keep_max = ((((lane * E) & K) != 0) != (((lane * E) & J) != 0));
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int32_t b = lane_xor<J / E>(a[e], addr_xor32);
+      const bool take_b = (a[e] > b) != keep_max;
+      a[e] = take_b ? b : a[e];
+    }
+  }
+}
+
+template <int E, int K, int J>
+__device__ __forceinline__ void bitonic_merge(int32_t (&a)[E], int lane, int32_t addr_xor32) {
+  bitonic_stage<E, K, J>(a, lane, addr_xor32);
+  if constexpr (J > 1) bitonic_merge<E, K, J / 2>(a, lane, addr_xor32);
+}
+
+template <int E, int K>
+__device__ __forceinline__ void bitonic_sort(int32_t (&a)[E], int lane, int32_t addr_xor32) {
+  if constexpr (K <= kWave * E) {
+    bitonic_merge<E, K, K / 2>(a, lane, addr_xor32);
+    bitonic_sort<E, K * 2>(a, lane, addr_xor32);
+  }
 }
 
 template <int E>
@@ -42,7 +119,6 @@ __global__ __launch_bounds__(kWave) void expand_kernel(
     const int32_t *row_ke, int64_t ke_stride, uint32_t rows, int32_t num_candidates,
     int32_t ratio, int32_t sbk, int32_t *sparse, int64_t sparse_stride, int32_t *end,
     int64_t end_stride) {
-  constexpr int N = kWave * E;
   const uint32_t row = blockIdx.x;
   if (row >= rows) return;
   const int lane = threadIdx.x;
@@ -57,7 +133,7 @@ __global__ __launch_bounds__(kWave) void expand_kernel(
   const int32_t base = static_cast<int32_t>(ks / sbk);
 
   int32_t a[E];
-  int32_t count = 0, last = -1;
+  int32_t n_valid = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int32_t i = lane * E + e;
@@ -65,43 +141,22 @@ __global__ __launch_bounds__(kWave) void expand_kernel(
     if (i < L) v = ratio == 2 ? static_cast<int64_t>(c[i >> 1]) * 2 + (i & 1) : c[i];
     const bool keep = i < L && v >= 0 && v < max_block;
     a[e] = keep ? static_cast<int32_t>(v) : kSentinel;
-    count += keep ? 1 : 0;
-    last = keep ? max(last, static_cast<int32_t>(v)) : last;
-  }
-  const int32_t n_valid = wave_sum_i32(count);
-  last = wave_max_i32(last);
-
-  // Bitonic sort of the N keys, ascending. Position i compares with i ^ j;
-  // within each k-sized run the direction is ascending when (i & k) == 0.
-#pragma unroll
-  for (int k = 2; k <= N; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j < E) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int p = e ^ j;
-          if (p > e) {
-            const int32_t i = lane * E + e;
-            const bool up = (i & k) == 0;
-            const int32_t lo = min(a[e], a[p]), hi = max(a[e], a[p]);
-            a[e] = up ? lo : hi;
-            a[p] = up ? hi : lo;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int32_t b = __shfl_xor(a[e], j / E);
-          const int32_t i = lane * E + e;
-          const bool up = (i & k) == 0;
-          const bool lower = (i & j) == 0;  // this position is the pair's first
-          a[e] = (up == lower) ? min(a[e], b) : max(a[e], b);
-        }
-      }
-    }
+    n_valid += __builtin_popcountll(__ballot(keep));  // uniform
   }
 
+  // Bitonic sort of the 64 * E keys, ascending.
+  const int32_t addr_xor32 = (lane ^ 32) << 2;
+  bitonic_sort<E, 2>(a, lane, addr_xor32);
+
+  // The last kept block is the key at sorted position n_valid - 1.
+  int32_t last = -1;
+  if (n_valid > 0) {
+    const int32_t pos = n_valid - 1;
+    int32_t v = a[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) v = (pos % E) == e ? a[e] : v;
+    last = __builtin_amdgcn_readlane(v, pos / E);
+  }
   const int32_t pad = n_valid > 0 ? last + base : base;
   int32_t *out = sparse + row * sparse_stride;
 #pragma unroll
