@@ -333,12 +333,37 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
   }
   if constexpr (kFmt == kFmtFp8) {
     // Non-packed fp8 cache with one fp32 per-tensor scale: the 512 B row at
-    // page + off*512 holds e4m3fn(r / scale), saturated to +-448. The
-    // quotient is one IEEE fp32 division (rounded once); the conversion then
+    // page + off*512 holds e4m3fn(r / scale), saturated to +-448, where r /
+    // scale is the IEEE fp32 quotient (rounded once); the conversion then
     // runs with a unit scale (UE8M0 byte 127 = 2^0), rounding to nearest even.
     float y[8];
+    const float s = fp8_scale;
+    if (s >= 0x1p-90f && s <= 0x1p90f) {
+      // The scale is uniform, so its reciprocal is formed once (correctly
+      // rounded) and each quotient by Markstein's method (P. Markstein, "IA-64
+      // and elementary functions", 2000: if rc is 1/s rounded to nearest and q
+      // is faithful, q + (a - s q) rc rounded to nearest is the correctly
+      // rounded a / s): q0 = a rc, one fused residual correction (faithful),
+      // a second (correctly rounded). a is first clamped to +-1024 s: any
+      // larger quotient saturates anyway, and the clamp keeps every
+      // intermediate finite; the residuals stay exact down to quotients of
+      // 2^-11, below which every result encodes as a signed zero. The sign
+      // is restored at the end for the zero quotients of -0 and tiny a.
+      const float rc = __fdiv_rn(1.0f, s);
+      const float lim = 1024.0f * s;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) y[k] = fminf(fmaxf(__fdiv_rn(f[k], fp8_scale), -448.0f), 448.0f);
+      for (int k = 0; k < 8; ++k) {
+        const float a = fminf(fmaxf(f[k], -lim), lim);
+        float q = a * rc;
+        q = fmaf(fmaf(-s, q, a), rc, q);
+        q = fmaf(fmaf(-s, q, a), rc, q);
+        y[k] = fminf(fmaxf(copysignf(q, f[k]), -448.0f), 448.0f);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        y[k] = fminf(fmaxf(__fdiv_rn(f[k], s), -448.0f), 448.0f);
+    }
     st<nt_data>(reinterpret_cast<u32x2 *>(page + off * 512u + lane * 8), encode_e4m3x8(y, 127u));
     return;
   }

@@ -337,20 +337,25 @@ def _kernel_bodies(asm: str) -> dict:
 
 def test_kernels_have_no_fma_and_no_packed_fp32():
     """No contraction: the rotation's products and sums are rounded one by
-    one. The only fused multiply-adds allowed are the five inside each IEEE
-    fp32 division sequence (ending in v_div_fixup_f32) of the fp8 cache."""
+    one. Fused multiply-adds appear only in the fp8 cache's insert, which
+    divides by the per-tensor scale: five inside each IEEE division sequence
+    (ending in v_div_fixup_f32) and four per element (32 per lane) in the
+    reciprocal path's two Markstein corrections. Every other kernel has none."""
     asm = KB.device_asm()
     code = "\n".join(l for l in asm.splitlines() if not l.lstrip().startswith((";", ".")))
     for op in ("v_mad_f32", "v_mac_f32", "v_fma_mix",
                "v_pk_fma_f32", "v_pk_mul_f32", "v_pk_add_f32"):
         assert op not in code, op
-    divs = 0
+    fp8_kernels = 0
     for name, ops in _kernel_bodies(asm).items():
         fma = sum(op.startswith(("v_fma_f32", "v_fmac_f32")) for op in ops)
         fixup = sum(op.startswith("v_div_fixup_f32") for op in ops)
-        assert fma == 5 * fixup, (name, fma, fixup)
-        divs += fixup
-    assert divs > 0  # the fp8 cache's kernel divides
+        if re.search(r"insert_kernelILi\d+ELi\d+ELi\d+ELi3E", name):  # the fp8 format
+            fp8_kernels += 1
+            assert fixup >= 9 and fma <= 5 * fixup + 32, (name, fma, fixup)
+        else:
+            assert fma == 0 and fixup == 0, (name, fma, fixup)
+    assert fp8_kernels > 0
     # fp32 denormals preserved for every kernel (mode 3 = keep inputs and outputs)
     modes = re.findall(r"\.amdhsa_float_denorm_mode_32\s+(\d+)", asm)
     assert modes and set(modes) == {"3"}

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from quantized_paged_kv_rope_amd import binding as B
 from quantized_paged_kv_rope_amd import workloads as W
 from tests import parity_util as P
@@ -149,5 +150,46 @@ def test_bf16_rounding_edges(record):
     else:
         d.insert()
         want = P.oracle_insert(case, case.initial_backing())
+    got = d.backing_host()
+    assert np.array_equal(got, want), P.first_diff(got, want)
+
+
+def test_fp8_quotient_ties_on_gpu():
+    """Scales s = fl32(x / T) for e4m3 midpoints T put the fp32 quotient
+    fl(x / s) exactly on T while the exact quotient lies beside it: the
+    kernel's division must round like IEEE fp32 division and the conversion
+    must then break the tie to the even code, as the oracle does. One token
+    (x in a NoPE dim, the rest zero) per scale."""
+    from fractions import Fraction
+
+    ties = [(1.0 + (2 * m + 1) / 16.0) * 2.0 ** k for m in range(8) for k in (-4, 0, 3, 6)]
+    mags = np.arange(0x3C00, 0x4400, 53, dtype=np.uint16)
+    xs = (mags.astype(np.uint32) << 16).view(np.float32)
+    cases = []
+    for T in ties:
+        sc = (xs.astype(np.float64) / T).astype(np.float32)
+        q = xs / sc
+        for i in np.nonzero(q == np.float32(T))[0]:
+            if Fraction(float(xs[i])) != Fraction(T) * Fraction(float(sc[i])):
+                cases.append((int(mags[i]), float(sc[i])))
+    assert len(cases) >= 100
+    cases = cases[:160]
+    n = len(cases)
+    case = W.custom_insert(4242, n, W.RECORD_FP8, 16, n // 16 + 2, max_pos=1, drop_frac=0.0)
+    kv = np.zeros((n, 512), np.uint16)
+    for t, (bits, _) in enumerate(cases):
+        kv[t, 7] = bits
+        kv[t, 300] = bits ^ 0x8000  # the negative too
+    case.kv_bits = kv
+    d = P.DeviceCase(case)
+    sc_dev = torch.empty(1, dtype=torch.float32, device="cuda")
+    want = case.initial_backing()
+    for t, (_, s) in enumerate(cases):
+        sc_dev.fill_(s)
+        B.kvrec_insert_full(d.kv[t:t + 1], d.k_cache, d.slots[t:t + 1], d.positions[t:t + 1],
+                            d.cos_sin, case.block_size, sc_dev)
+        oracle.insert_full(kv[t:t + 1], want, case.num_blocks, case.page_stride,
+                           case.block_size, case.record, case.slot_mapping[t:t + 1],
+                           case.positions[t:t + 1], case.cos_sin, s)
     got = d.backing_host()
     assert np.array_equal(got, want), P.first_diff(got, want)

@@ -389,3 +389,40 @@ def test_config_topk_gather_sampled():
     assert checked >= 4 * 2048 * 0.9
     del backing, k_cache, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("record", [528, 584])
+def test_largest_page(record):
+    """One page just under 2^31 bytes (the ABI's limit: in-page offsets are
+    32-bit on the device), written at its last 64 slots and gathered back:
+    the rows and scale bytes near the end of the page equal the oracle's."""
+    limit = 2 ** 31
+    bs = limit // record - 1
+    stride = W.page_stride_for(record, bs)
+    assert stride < limit and bs * record < limit
+    n = 64
+    rng = np.random.default_rng(2 ** 20 + record)
+    x = rng.standard_normal((n, 512), dtype=np.float32) * rng.uniform(0.1, 10, (n, 1)).astype(np.float32)
+    slots = (bs - n + rng.permutation(n)).astype(np.int64)
+    slots[5] = -1
+    case = W.InsertCase("largest_page", record, bs, 1, stride, W.to_bf16_bits(x), slots,
+                        rng.integers(0, 4096, n).astype(np.int64), W.rope_table(4096), None)
+    backing = torch.zeros(stride, dtype=torch.uint8, device="cuda")
+    _, kc = B.alloc_cache(1, bs, record, stride, backing=backing)
+    B.kvrec_insert(P.dev_bf16(case.kv_bits), kc, P.dev(slots), P.dev(case.positions),
+                   P.dev(case.cos_sin), bs)
+    idx = np.where(slots >= 0, slots, -1).astype(np.int32)
+    out = P.host_bits(B.kvrec_gather(kc, P.dev(idx)))
+    torch.cuda.synchronize()
+    want = np.zeros(stride, np.uint8)
+    oracle.insert(case.kv_bits, want, 1, stride, bs, record, slots, case.positions, case.cos_sin)
+    row_bytes, scale_bytes = (512, 16) if record == 528 else (576, 8)
+    lo_data, lo_scale = (bs - n) * row_bytes, bs * row_bytes + (bs - n) * scale_bytes
+    got_data = backing[lo_data: bs * row_bytes].cpu().numpy()
+    got_scale = backing[lo_scale: bs * row_bytes + bs * scale_bytes].cpu().numpy()
+    assert np.array_equal(got_data, want[lo_data: bs * row_bytes])
+    assert np.array_equal(got_scale, want[lo_scale: bs * row_bytes + bs * scale_bytes])
+    want_out = oracle.gather(want, 1, stride, bs, record, idx)
+    assert np.array_equal(out, want_out), P.first_diff(out, want_out)
+    del backing, kc
+    torch.cuda.empty_cache()
