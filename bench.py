@@ -98,8 +98,9 @@ def all_configs_report(dev, out=sys.stderr) -> list:
 
     flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
 
-    def cold(fn, reps=10):
-        fn()
+    def cold(fn, reps=50):
+        for _ in range(5):
+            fn()
         ts = []
         for _ in range(reps):
             flush.sum(dtype=torch.int64)  # reads 1 GiB: caches left holding clean lines
@@ -109,7 +110,7 @@ def all_configs_report(dev, out=sys.stderr) -> list:
             e1.record()
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e3)
-        return float(np.median(ts))
+        return np.percentile(ts, [50, 10, 90])
 
     def replayed(fn, reps=20):
         fn()
@@ -134,11 +135,13 @@ def all_configs_report(dev, out=sys.stderr) -> list:
     rows = []
 
     def add(workload, op, n, valid, nbytes, fn):
-        c, r = cold(fn), replayed(fn)
+        (c, c10, c90), r = cold(fn), replayed(fn)
         rows.append({"workload": workload, "op": op, "rows": n, "valid": valid,
-                     "algorithmic_bytes": nbytes, "cold_us": c, "replayed_us": r,
+                     "algorithmic_bytes": nbytes, "cold_us": c, "cold_p10_us": c10,
+                     "cold_p90_us": c90, "replayed_us": r,
                      "cold_GBps": nbytes / c / 1e3, "replayed_GBps": nbytes / r / 1e3,
-                     "tokens_per_s_replayed": n / r * 1e6})
+                     "tokens_per_s_replayed": n / r * 1e6,
+                     "valid_tokens_per_s_replayed": valid / r * 1e6})
 
     cases = [W.mixed_1024(), W.decode_16384(), W.prefill_262144(), W.legacy_65536()]
     for case in cases:
@@ -230,10 +233,11 @@ def all_configs_report(dev, out=sys.stderr) -> list:
         lambda: B.kvrec_gather(kc, idx, out=o))
     del backing, kc, o, flush
     torch.cuda.empty_cache()
-    print(f"{'workload':28s} {'op':14s} {'rows':>7s} {'cold us':>8s} {'GB/s':>6s} "
-          f"{'%peak':>6s} {'replay us':>9s} {'GB/s':>6s} {'%peak':>6s}", file=out)
+    print(f"{'workload':28s} {'op':14s} {'rows':>7s} {'cold us':>8s} {'p10-p90':>11s} "
+          f"{'GB/s':>6s} {'%peak':>6s} {'replay us':>9s} {'GB/s':>6s} {'%peak':>6s}", file=out)
     for r in rows:
         print(f"{r['workload']:28s} {r['op']:14s} {r['rows']:7d} {r['cold_us']:8.1f} "
+              f"{r['cold_p10_us']:5.1f}-{r['cold_p90_us']:<5.1f} "
               f"{r['cold_GBps']:6.0f} {100 * r['cold_GBps'] / HBM_PEAK_GBPS:5.1f}% "
               f"{r['replayed_us']:9.1f} {r['replayed_GBps']:6.0f} "
               f"{100 * r['replayed_GBps'] / HBM_PEAK_GBPS:5.1f}%", file=out, flush=True)
@@ -364,9 +368,13 @@ def main() -> int:
         },
         "kernels": {
             "insert": {"avg_us": ins_s * 1e6, "p50_us": float(np.median(ins_ms)) * 1e3,
+                                    "p10_us": float(np.percentile(ins_ms, 10)) * 1e3,
+                                    "p90_us": float(np.percentile(ins_ms, 90)) * 1e3,
                                     "GBps": ins_gbps, "frac_of_peak": ins_gbps / HBM_PEAK_GBPS,
                                     "tokens_per_s": TOKENS / ins_s},
             "gather": {"avg_us": gat_s * 1e6, "p50_us": float(np.median(gat_ms)) * 1e3,
+                                    "p10_us": float(np.percentile(gat_ms, 10)) * 1e3,
+                                    "p90_us": float(np.percentile(gat_ms, 90)) * 1e3,
                                     "GBps": gat_gbps, "frac_of_peak": gat_gbps / HBM_PEAK_GBPS,
                                     "tokens_per_s": TOKENS / gat_s,
                                     "algorithmic_bytes_per_launch": gat_bytes},
