@@ -11,13 +11,24 @@
 // Shape. One wave64 per row. The L = K * RATIO expanded blocks are held in
 // registers, E = max(L, 64) / 64 per lane (lane l holds positions
 // l*E .. l*E + E-1); positions past L and dropped blocks hold a sentinel
-// larger than any kept block. A bitonic network sorts the 64*E keys:
-// exchanges at distance < E stay inside a lane; the others read the partner
-// lane by DPP (lane distances 1..8), ds_swizzle (16) or ds_bpermute (32), and
-// keep the smaller or larger key by one compare and one select, the direction
-// being a per-stage property of the lane. The kept count comes from ballots;
-// the kept blocks then occupy positions 0 .. n_valid-1 in order, and each
-// lane writes its E outputs.
+// larger than any kept block. The kept count comes from ballots. Two ways to
+// order the kept blocks, chosen per row (the choice is uniform in the wave):
+//
+// - Rank sort, when the row has at most kRankMaxBlocks blocks and its kept
+//   blocks are distinct (the candidates of a top-k are): each kept block sets
+//   its bit in a bitmap in LDS; a prefix sum of the words' popcounts gives
+//   every block its rank, the number of kept blocks below it; each block is
+//   written to its rank in an LDS row and read back in order. The bitmap's
+//   popcount equals the kept count exactly when no block repeats, so a
+//   repeated block sends the row to the network below.
+// - A bitonic network otherwise: exchanges at distance < E stay inside a
+//   lane; the others read the partner lane by DPP (lane distances 1..8),
+//   ds_swizzle (16) or ds_bpermute (32), and keep the smaller or larger key
+//   by one compare and one select, the direction being a per-stage property
+//   of the lane.
+//
+// Either way the kept blocks end at positions 0 .. n_valid-1 in ascending
+// order, and each lane writes its E outputs.
 #include "kvrec_launch.h"
 
 namespace kvrec {
@@ -31,8 +42,15 @@ constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]: lane l ^ 1
 constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]: lane l ^ 2
 constexpr int kQuadReverse = 0x1B;   // quad_perm [3,2,1,0]: lane l ^ 3
 constexpr int kHalfRowMirror = 0x141;  // lane l ^ 7 within 8 lanes
-constexpr int kRowMirror = 0x140;      // lane l ^ 15 within 16 lanes
+constexpr int kRowRotate8 = 0x128;     // row_ror:8, i.e. lane l ^ 8 within 16 lanes
+constexpr int kRowShr1 = 0x111;        // row_shr:n is 0x110 + n: lane l - n within a row
 constexpr int kSwizzleXor16 = 0x1F | (16 << 10);
+
+// Rank sort limits: rows of up to 16384 blocks (a 512-word bitmap, at most 8
+// words per lane).
+constexpr int kRankMaxBlocks = 16384;
+constexpr int kRankWords = kRankMaxBlocks / 32;
+
 
 template <int Ctrl>
 __device__ __forceinline__ int32_t dpp(int32_t v) {
@@ -40,14 +58,14 @@ __device__ __forceinline__ int32_t dpp(int32_t v) {
 }
 
 // The value held by lane l ^ D. Distances 1..8 are DPP moves (VALU, no LDS
-// round trip): xor 4 = (xor 7) then (xor 3), xor 8 = (xor 15) then (xor 7);
-// 16 is a ds_swizzle within 32 lanes, 32 a ds_bpermute.
+// round trip): xor 4 = (xor 7) then (xor 3), xor 8 = a rotation of the
+// 16-lane row by 8; 16 is a ds_swizzle within 32 lanes, 32 a ds_bpermute.
 template <int D>
 __device__ __forceinline__ int32_t lane_xor(int32_t v, int32_t addr_xor32) {
   if constexpr (D == 1) return dpp<kQuadXor1>(v);
   else if constexpr (D == 2) return dpp<kQuadXor2>(v);
   else if constexpr (D == 4) return dpp<kQuadReverse>(dpp<kHalfRowMirror>(v));
-  else if constexpr (D == 8) return dpp<kHalfRowMirror>(dpp<kRowMirror>(v));
+  else if constexpr (D == 8) return dpp<kRowRotate8>(v);
   else if constexpr (D == 16) return __builtin_amdgcn_ds_swizzle(v, kSwizzleXor16);
   else return __builtin_amdgcn_ds_bpermute(addr_xor32, v);
 }
@@ -113,6 +131,70 @@ __device__ __forceinline__ void bitonic_sort(int32_t (&a)[E], int lane, int32_t 
   }
 }
 
+// Exclusive prefix sum of v over the 64 lanes; *total receives the sum over
+// all lanes. Inclusive sums within each 16-lane row by four DPP shifts (a
+// lane whose source lies before its row adds 0), then each row adds the
+// totals of the rows before it.
+__device__ __forceinline__ uint32_t wave_exclusive_sum(uint32_t v, int lane, uint32_t *total) {
+  uint32_t s = v;
+  s += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int32_t>(s), kRowShr1, 0xF, 0xF, false));
+  s += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int32_t>(s), kRowShr1 + 1, 0xF, 0xF, false));
+  s += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int32_t>(s), kRowShr1 + 3, 0xF, 0xF, false));
+  s += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int32_t>(s), kRowShr1 + 7, 0xF, 0xF, false));
+  const uint32_t r0 = __builtin_amdgcn_readlane(s, 15), r1 = __builtin_amdgcn_readlane(s, 31),
+                 r2 = __builtin_amdgcn_readlane(s, 47), r3 = __builtin_amdgcn_readlane(s, 63);
+  *total = r0 + r1 + r2 + r3;
+  const uint32_t before = lane < 16 ? 0u : lane < 32 ? r0 : lane < 48 ? r0 + r1 : r0 + r1 + r2;
+  return s + before - v;
+}
+
+// Rank sort of the kept keys of one row into ascending order (positions
+// 0 .. n_valid-1 of a[]), for keys in [0, 32 * words) with words <= kRankWords.
+// Returns false, leaving a[] as it was, when a key repeats.
+template <int E>
+__device__ __forceinline__ bool rank_sort(int32_t (&a)[E], int lane, uint32_t words,
+                                          int32_t n_valid, uint2 *bitmap, int32_t *sorted) {
+  // Words [0, 64 q) are used, lane l owning l*q .. l*q + q-1; those past
+  // `words` stay zero.
+  // The loops over a lane's words run q times (q is uniform, 1 for rows of
+  // up to 2048 blocks).
+  const uint32_t q = (words + kWave - 1) / kWave;
+  uint2 *mine = bitmap + lane * q;
+#pragma unroll 1
+  for (uint32_t j = 0; j < q; ++j) mine[j].x = 0;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (a[e] != kSentinel) atomicOr(&bitmap[a[e] >> 5].x, 1u << (a[e] & 31));
+  __syncthreads();
+  uint32_t count = 0;
+#pragma unroll 1
+  for (uint32_t j = 0; j < q; ++j) count += __builtin_popcount(mine[j].x);
+  uint32_t total;
+  uint32_t below = wave_exclusive_sum(count, lane, &total);
+  if (total != static_cast<uint32_t>(n_valid)) return false;  // uniform
+#pragma unroll 1
+  for (uint32_t j = 0; j < q; ++j) {
+    const uint32_t w = mine[j].x;
+    mine[j].y = below;
+    below += __builtin_popcount(w);
+  }
+  __syncthreads();
+  // Rank = kept blocks in earlier words + set bits below the key in its word.
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (a[e] != kSentinel) {
+      const uint2 wp = bitmap[a[e] >> 5];
+      const uint32_t rank = wp.y + __builtin_popcount(wp.x & ((1u << (a[e] & 31)) - 1u));
+      sorted[rank] = a[e];
+    }
+  __syncthreads();
+  // Positions n_valid and above are never read from a[] afterwards.
+#pragma unroll
+  for (int e = 0; e < E; ++e) a[e] = sorted[lane * E + e];
+  return true;
+}
+
 template <int E>
 __global__ __launch_bounds__(kWave) void expand_kernel(
     const int32_t *cand, int64_t cand_stride, const int32_t *row_ks, int64_t ks_stride,
@@ -123,30 +205,53 @@ __global__ __launch_bounds__(kWave) void expand_kernel(
   if (row >= rows) return;
   const int lane = threadIdx.x;
   const int32_t *c = cand + row * cand_stride;
-  // Exact integer arithmetic (64-bit where an int32 sum could wrap); every
-  // stored value fits in int32. ks and ke are >= 0 (a precondition).
-  const int64_t ks = row_ks[row * ks_stride];
-  const int64_t ke = row_ke[row * ke_stride];
+  // ks, ke >= 0 (a precondition), so kv_len < 2^31 and max_block <= 2^28;
+  // SBK is 8 or 16, a power of two.
+  const int32_t ks = row_ks[row * ks_stride];
+  const int32_t ke = row_ke[row * ke_stride];
   const int32_t L = num_candidates * ratio;
-  const int64_t kv_len = ke - ks > 0 ? ke - ks : 0;
-  const int64_t max_block = (kv_len + sbk - 1) / sbk;
-  const int32_t base = static_cast<int32_t>(ks / sbk);
+  const uint32_t sbk_shift = sbk == 16 ? 4u : 3u;
+  const uint32_t kv_len = ke > ks ? static_cast<uint32_t>(ke - ks) : 0u;
+  const uint32_t max_block = (kv_len + static_cast<uint32_t>(sbk) - 1u) >> sbk_shift;
+  const int32_t base = ks >> sbk_shift;
+  const uint32_t split = static_cast<uint32_t>(ratio) - 1u;  // 1 when each candidate is 2 blocks
 
+  // All candidate loads are issued before any is used: positions past L
+  // read candidate K-1 (a valid address) and are dropped below.
+  // (32-bit byte offsets from the row's base: K <= 1024.)
+  const char *crow = reinterpret_cast<const char *>(c);
+  int32_t cv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t idx = static_cast<uint32_t>(min(lane * E + e, L - 1)) >> split;
+    cv[e] = *reinterpret_cast<const int32_t *>(crow + idx * 4u);
+  }
+  // Block of position i: (c << split) | (i & split). A candidate c >= 0 is
+  // kept when that block is below max_block; c itself is checked first so
+  // the shift cannot wrap (c < max_block <= 2^28), and negative c fail it as
+  // unsigned values.
   int32_t a[E];
   int32_t n_valid = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int32_t i = lane * E + e;
-    int64_t v = -1;
-    if (i < L) v = ratio == 2 ? static_cast<int64_t>(c[i >> 1]) * 2 + (i & 1) : c[i];
-    const bool keep = i < L && v >= 0 && v < max_block;
-    a[e] = keep ? static_cast<int32_t>(v) : kSentinel;
-    n_valid += __builtin_popcountll(__ballot(keep));  // uniform
+    const uint32_t cu = static_cast<uint32_t>(cv[e]);
+    const uint32_t block = (cu << split) | (static_cast<uint32_t>(i) & split);
+    const bool keep = i < L && cu < max_block && block < max_block;
+    a[e] = keep ? static_cast<int32_t>(block) : kSentinel;
+    n_valid += __builtin_popcountll(__builtin_amdgcn_ballot_w64(keep));  // uniform
   }
 
-  // Bitonic sort of the 64 * E keys, ascending.
-  const int32_t addr_xor32 = (lane ^ 32) << 2;
-  bitonic_sort<E, 2>(a, lane, addr_xor32);
+  __shared__ uint2 bitmap[kRankWords];
+  __shared__ __align__(16) int32_t sorted[kWave * E];
+  bool done = false;
+  if (max_block <= kRankMaxBlocks)  // uniform
+    done = rank_sort<E>(a, lane, (max_block + 31u) / 32u, n_valid, bitmap, sorted);
+  if (!done) {
+    // Bitonic sort of the 64 * E keys, ascending.
+    const int32_t addr_xor32 = (lane ^ 32) << 2;
+    bitonic_sort<E, 2>(a, lane, addr_xor32);
+  }
 
   // The last kept block is the key at sorted position n_valid - 1.
   int32_t last = -1;
@@ -158,11 +263,13 @@ __global__ __launch_bounds__(kWave) void expand_kernel(
     last = __builtin_amdgcn_readlane(v, pos / E);
   }
   const int32_t pad = n_valid > 0 ? last + base : base;
-  int32_t *out = sparse + row * sparse_stride;
+  char *out = reinterpret_cast<char *>(sparse + row * sparse_stride);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int32_t i = lane * E + e;
-    if (i < L) out[i] = i < n_valid ? a[e] + base : pad;
+    if (i < L)
+      *reinterpret_cast<int32_t *>(out + static_cast<uint32_t>(i) * 4u) =
+          i < n_valid ? a[e] + base : pad;
   }
   if (lane == 0) {
     const int64_t last_start = static_cast<int64_t>(last) * sbk + ks;

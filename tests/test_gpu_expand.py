@@ -114,3 +114,51 @@ def test_sparse_expand_16384():
     want = oracle.expand_candidates(x.cand, x.row_ks, x.row_ke, x.ratio, x.sparse_block)
     assert np.array_equal(got[0], want[0])
     assert np.array_equal(got[1], want[1])
+
+
+# Blocks per row (max_block) around the kernel's choices: bitmap words per lane
+# 1..8 (up to 16384 blocks) take the rank sort, more blocks the network.
+MAX_BLOCKS = [1, 2, 31, 32, 33, 64, 65, 2047, 2048, 2049, 4095, 4096, 4097, 8191, 8192, 12000,
+              16383, 16384, 16385, 16416, 40000, 2 ** 20]
+
+
+def _path_rows(k, ratio, sbk, rng):
+    """One row per (max_block, kind): kind 0 distinct candidates, 1 a kept
+    candidate repeated, 2 distinct kept candidates with repeats among the
+    dropped ones (-1 and one out-of-range value)."""
+    cand, ks, ke = [], [], []
+    for mb in MAX_BLOCKS:
+        for kind in range(3):
+            kv_len = mb * sbk - int(rng.integers(0, sbk))
+            start = int(rng.integers(0, 2 ** 31 - 1 - kv_len))
+            hi = -(-mb // ratio)  # candidates with a block below max_block
+            span = hi + 3
+            row = rng.choice(span, min(k, span), replace=False).astype(np.int64)
+            row = np.concatenate([row, np.full(k - len(row), -1)])
+            row[rng.random(k) < 0.1] = -1
+            kept = np.nonzero((row >= 0) & (row < hi))[0]
+            if kind == 1 and len(kept) >= 2:
+                row[kept[-1]] = row[kept[0]]
+            if kind == 2:
+                drop = np.nonzero((row < 0) | (row >= hi))[0]
+                row[drop[: len(drop) // 2]] = hi + 7
+            cand.append(row.astype(np.int32))
+            ks.append(start)
+            ke.append(start + kv_len)
+    return np.stack(cand), np.array(ks, np.int32), np.array(ke, np.int32)
+
+
+@pytest.mark.parametrize("k,ratio", [(16, 1), (32, 2), (64, 2), (128, 2), (256, 1), (256, 2),
+                                     (512, 2), (1024, 1)])
+@pytest.mark.parametrize("sbk", [8, 16])
+def test_rank_sort_and_network_paths(k, ratio, sbk):
+    """Rows on both sides of the rank sort's limits (blocks per row, bitmap
+    words per lane, repeated kept blocks), all in one launch so the two paths
+    run side by side; every output compared."""
+    rng = np.random.default_rng(9000 + k + ratio + sbk)
+    cand, ks, ke = _path_rows(k, ratio, sbk, rng)
+    got = _gpu(cand, ks, ke, ratio, sbk)
+    want = oracle.expand_candidates(cand, ks, ke, ratio, sbk)
+    bad = np.argwhere(got[0] != want[0])
+    assert len(bad) == 0, (bad[:5], [MAX_BLOCKS[r // 3] for r in bad[:5, 0]])
+    assert np.array_equal(got[1], want[1])
