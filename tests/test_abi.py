@@ -325,6 +325,29 @@ def test_python_binding_rejects_cpu_tensors():
                             torch.zeros(8, 64), 4)
 
 
+def test_python_binding_rejects_cpu_tensors_widened_calls():
+    import torch
+
+    q = torch.zeros(4, 2, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="on a GPU"):
+        B.kvrec_qnorm_rope_insert(q, torch.zeros(4, 512, dtype=torch.bfloat16),
+                                  torch.zeros(1, 4, 528, dtype=torch.uint8),
+                                  torch.zeros(4, dtype=torch.int64), torch.zeros(4, dtype=torch.int64),
+                                  torch.zeros(8, 64), 4)
+    with pytest.raises(ValueError, match="on a GPU"):
+        B.kvrec_expand_candidates(torch.zeros(2, 8, dtype=torch.int32),
+                                  torch.zeros(2, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
+                                  2, 8)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every entry point raises: there is no other
+    path to fall back to."""
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        B.load_library(str(tmp_path / "libkvrec.so"))
+
+
 def _kernel_bodies(asm: str) -> dict:
     bodies = {}
     for name in re.findall(r"^(_Z\S+):", asm, re.M):
