@@ -254,6 +254,32 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+# hipDeviceAttribute_t values (hip_runtime_api.h, ROCm 7).
+_HIP_ATTR = {"shader_clock_khz": 5, "memory_bus_width_bits": 59, "memory_clock_khz": 60,
+             "compute_units": 63}
+
+
+def device_info() -> dict:
+    """What the device reports about itself (name, arch, CU count, clocks,
+    memory bus width), read through the HIP runtime torch loaded. The HBM
+    peak used for `frac` stays the published 8 TB/s: the reported memory
+    clock is not the HBM3E data rate."""
+    import ctypes
+
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    info = {"name": props.name, "arch": props.gcnArchName,
+            "total_memory_GiB": round(props.total_memory / 2 ** 30, 1)}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+    except OSError:
+        return info
+    for key, attr in _HIP_ATTR.items():
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, torch.cuda.current_device()) == 0:
+            info[key] = v.value
+    return info
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,6 +406,7 @@ def main() -> int:
                                     "algorithmic_bytes_per_launch": gat_bytes},
         },
         "kernel_source_sha256_16": kernel_source_hash(),
+        "device": device_info(),
     }
     if copy_gbps is not None:
         result["device_copy_GBps"] = copy_gbps

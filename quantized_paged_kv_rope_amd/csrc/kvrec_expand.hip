@@ -51,7 +51,6 @@ constexpr int kSwizzleXor16 = 0x1F | (16 << 10);
 constexpr int kRankMaxBlocks = 16384;
 constexpr int kRankWords = kRankMaxBlocks / 32;
 
-
 template <int Ctrl>
 __device__ __forceinline__ int32_t dpp(int32_t v) {
   return __builtin_amdgcn_mov_dpp(v, Ctrl, 0xF, 0xF, true);
@@ -80,8 +79,6 @@ __device__ __forceinline__ void bitonic_stage(int32_t (&a)[E], int lane, int32_t
   if constexpr (J < E) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      constexpr int dummy = 0;
-      (void)dummy;
       const int p = e ^ J;
       if (p > e) {
         if constexpr (K < E) {
@@ -135,12 +132,18 @@ __device__ __forceinline__ void bitonic_sort(int32_t (&a)[E], int lane, int32_t 
 // all lanes. Inclusive sums within each 16-lane row by four DPP shifts (a
 // lane whose source lies before its row adds 0), then each row adds the
 // totals of the rows before it.
+template <int N>
+__device__ __forceinline__ uint32_t row_shr(uint32_t v) {  // 0 where l - N leaves the row
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int32_t>(v), kRowShr1 + N - 1, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ uint32_t wave_exclusive_sum(uint32_t v, int lane, uint32_t *total) {
   uint32_t s = v;
-  s += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int32_t>(s), kRowShr1, 0xF, 0xF, false));
-  s += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int32_t>(s), kRowShr1 + 1, 0xF, 0xF, false));
-  s += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int32_t>(s), kRowShr1 + 3, 0xF, 0xF, false));
-  s += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int32_t>(s), kRowShr1 + 7, 0xF, 0xF, false));
+  s += row_shr<1>(s);
+  s += row_shr<2>(s);
+  s += row_shr<4>(s);
+  s += row_shr<8>(s);
   const uint32_t r0 = __builtin_amdgcn_readlane(s, 15), r1 = __builtin_amdgcn_readlane(s, 31),
                  r2 = __builtin_amdgcn_readlane(s, 47), r3 = __builtin_amdgcn_readlane(s, 63);
   *total = r0 + r1 + r2 + r3;
@@ -155,9 +158,8 @@ template <int E>
 __device__ __forceinline__ bool rank_sort(int32_t (&a)[E], int lane, uint32_t words,
                                           int32_t n_valid, uint2 *bitmap, int32_t *sorted) {
   // Words [0, 64 q) are used, lane l owning l*q .. l*q + q-1; those past
-  // `words` stay zero.
-  // The loops over a lane's words run q times (q is uniform, 1 for rows of
-  // up to 2048 blocks).
+  // `words` stay zero. The loops over a lane's words run q times (q is
+  // uniform, 1 for rows of up to 2048 blocks).
   const uint32_t q = (words + kWave - 1) / kWave;
   uint2 *mine = bitmap + lane * q;
 #pragma unroll 1
