@@ -45,20 +45,27 @@ PROFILE_PMC = os.path.join(ROOT, "profiles", "insert_mxfp8_prefill_262144_pmc.tx
 KERNEL_SRC = os.path.join(ROOT, "quantized_paged_kv_rope_amd", "csrc", "kvrec_kernels.hip")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_code_hash(path: str = KERNEL_SRC) -> str:
+    """sha256[:16] of a kernel source's code: comments removed and every run
+    of whitespace made one space, so that an edit of comments or layout keeps
+    the hash and any change to the code changes it."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def counter_traffic():
     """HBM bytes per insert launch from the committed rocprofv3 counter
-    summary, or None if there is none or the kernel source changed since."""
+    summary, or None if there is none or the kernel code changed since."""
     if not os.path.exists(PROFILE_PMC):
         return None
     text = open(PROFILE_PMC).read()
-    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m = re.search(r"kernel_code_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != kernel_source_hash():
+    if not m or not t or m.group(1) != kernel_code_hash():
         return None
     return float(t.group(1))
 
@@ -405,7 +412,7 @@ def main() -> int:
                                     "tokens_per_s": TOKENS / gat_s,
                                     "algorithmic_bytes_per_launch": gat_bytes},
         },
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_code_sha256_16": kernel_code_hash(),
         "device": device_info(),
     }
     if copy_gbps is not None:

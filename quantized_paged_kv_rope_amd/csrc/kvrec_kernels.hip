@@ -1,7 +1,9 @@
 // kvrec_kernels.hip - gfx950 (MI355X, CDNA4) kernels of the paged KV-record
-// codec: fused RoPE + MXFP8 (or legacy) quantise + paged insert, the same
-// insert into the non-packed bf16 and fp8 caches, and the paged
-// dequantise-and-gather.
+// codec: fused RoPE + MXFP8 (or legacy) quantise + paged insert, with the
+// compressed-KV variants (interleaved or no rotation, ratio gate, amax floor,
+// NaN sanitising); the same insert into the non-packed bf16 and fp8 caches;
+// the attention write (per-head q RMSNorm + RoPE beside the insert); and the
+// paged dequantise-and-gather.
 //
 // Sources (page titles; sections as named on the pages):
 //   [MXFP8 record] vLLM PR #56893 report, "[Model][DSv4.1] Store the whole KV
@@ -29,8 +31,10 @@
 // Latency. Every load that depends on nothing (the kv row, the slot, the
 // position) is issued at once; only the cos/sin row waits for the position.
 // The kv row is loaded before the slot is known, so a skipped token costs one
-// wasted 1 KB read but no serialised round trip. Streamed data uses
-// non-temporal loads and stores (it is touched once).
+// wasted 1 KB read but no serialised round trip. The bf16 rows read by the
+// insert and written by the gather are non-temporal (touched once); records
+// and cos/sin rows go through the caches (the launch configuration below
+// gives the measured reasons).
 //
 // Bit-exactness. Built with -ffp-contract=off (no FMA: the rotation is two
 // rounded products and one rounded add/subtract, in that order) and with fp32
