@@ -220,7 +220,7 @@ static uint8_t quantise_group(const float *r, int first, int width, float amax_f
 /* Token count and slot skip: [KV-only op, 实现拆解 1 and 风险与影响];        */
 /* negative slot -> nothing written [MXFP8 record, 关键源码片段].             */
 /* Guard (a reading): a slot >= num_blocks*block_size or a position outside  */
-/* [0, max_pos) also skips the token.                                       */
+/* [0, max_pos) also skips the token (a position only where it is read).    */
 /*                                                                          */
 /* MXFP8 record (528 B/token) [MXFP8 record, 功能与动机 and 关键源码片段]:    */
 /*   page = slot / block_size, off = slot % block_size;                     */
@@ -265,6 +265,10 @@ int orc_insert_ex(const uint16_t *kv, int64_t n, uint8_t *cache, int64_t num_blo
   if (ratio < 1 || opts->rope < ORC_ROPE_NEOX || opts->rope > ORC_ROPE_NONE) return -1;
   /* positions (and the table) may be absent only with no rotation and ratio 1 */
   if (positions == NULL && (opts->rope != ORC_ROPE_NONE || ratio != 1)) return -1;
+  /* With no rotation and ratio 1 the positions serve nothing (no table row,
+   * no gate): they are not read, so no position, in range or not, skips a
+   * token. */
+  if (opts->rope == ORC_ROPE_NONE && ratio == 1) positions = NULL;
 
   for (t = 0; t < n; ++t) {
     float r[HEAD_DIM];

@@ -682,3 +682,29 @@ def test_rotation_free_insert_without_positions():
     with pytest.raises(ValueError):
         oracle.insert(case.kv_bits, b, 4, case.page_stride, 16, 528, case.slot_mapping, None, None,
                       rope="interleaved")
+
+
+@pytest.mark.parametrize("record", [528, 584])
+def test_rotation_free_ratio1_does_not_read_positions(record):
+    """With no rotation and ratio 1 the positions take no part (no table row,
+    no gate), so out-of-range ones skip nothing: the result equals the
+    insert without positions. With ratio 2 they are read again, and an
+    out-of-range position skips its token."""
+    case = W.custom_insert(93 + record, 60, record, 16, 5)
+    none = case.initial_backing()
+    oracle.insert(case.kv_bits, none, 5, case.page_stride, 16, record, case.slot_mapping, None,
+                  None, rope="none")
+    bad = np.array([-5, 10 ** 6, 3] * 20, np.int64)
+    got = case.initial_backing()
+    oracle.insert(case.kv_bits, got, 5, case.page_stride, 16, record, case.slot_mapping, bad,
+                  W.rope_table(4), rope="none")
+    assert np.array_equal(got, none)
+    gated = case.initial_backing()
+    oracle.insert(case.kv_bits, gated, 5, case.page_stride, 16, record, case.slot_mapping, bad,
+                  W.rope_table(4), rope="none", compress_ratio=2)
+    kept = case.slot_mapping[(bad == 3) & (case.slot_mapping >= 0)]
+    want = case.initial_backing()
+    sel = np.isin(case.slot_mapping, kept)
+    oracle.insert(case.kv_bits[sel], want, 5, case.page_stride, 16, record,
+                  case.slot_mapping[sel], None, None, rope="none")
+    assert np.array_equal(gated, want)
