@@ -82,3 +82,47 @@ def test_random_configuration(seed):
         out = d.gather(idx)
         want_g = P.oracle_gather(case, want, idx)
         assert np.array_equal(out, want_g), (case.name, P.first_diff(out, want_g))
+
+
+QKV_CASES = 24
+
+
+@pytest.mark.parametrize("seed", range(QKV_CASES))
+def test_random_attention_write(seed):
+    """The attention write over random head counts, eps, norm on or off,
+    both packed records, odd block sizes, skipped and out-of-range slots and
+    positions, and in-place or separate q output: cache bytes exact, q rows
+    within the fp32 error bound (tests/test_gpu_qside.py derives it), rows
+    of out-of-range positions left as they were."""
+    import oracle
+    from tests import test_gpu_qside as Q
+
+    rng = np.random.default_rng(72000 + seed)
+    record = int(rng.choice([W.RECORD_MXFP8, W.RECORD_LEGACY]))
+    bs = int(rng.choice([1, 5, 16, 64, 130]))
+    n = int(rng.integers(1, 400))
+    heads = int(rng.choice([1, 2, 3, 7, 16, 33, 128]))
+    nb = n // bs + 2
+    max_pos = int(rng.integers(2, 3000))
+    case = W.custom_insert(5000 + seed, n, record, bs, nb, max_pos=max_pos,
+                           drop_frac=float(rng.uniform(0.0, 0.3)), scale_rows=True)
+    bad = rng.random(n) < 0.05
+    case.positions[bad] = rng.choice([-2, max_pos, max_pos + 100], int(bad.sum()))
+    x = rng.standard_normal((n, heads, 512)).astype(np.float32)
+    x *= (10.0 ** rng.uniform(-3, 3, (n, heads, 1))).astype(np.float32)
+    x[rng.random((n, heads)) < 0.02] = 0.0  # all-zero heads
+    eps = float(rng.choice([1e-6, 1e-5, 1e-2]))
+    norm = bool(rng.integers(2))
+    in_place = bool(rng.integers(2))
+    aw = W.AttentionWrite(f"rand_qkv_{seed}", W.to_bf16_bits(x), eps, case)
+    sentinel = np.full_like(aw.q_bits, 0x1234)
+    got_q, got_cache = Q._run(aw, apply_norm=norm, in_place=in_place, q_out_init=sentinel)
+    want_cache = P.oracle_insert(case, case.initial_backing())
+    assert np.array_equal(got_cache, want_cache), P.first_diff(got_cache, want_cache)
+    init = aw.q_bits.copy() if in_place else sentinel.copy()
+    want_q = oracle.qnorm_rope(aw.q_bits, case.positions, case.cos_sin, eps, norm, out=init)
+    ok = (case.positions >= 0) & (case.positions < max_pos)
+    assert np.array_equal(got_q[~ok], want_q[~ok])
+    if ok.any():
+        Q._check_q(got_q[ok], want_q[ok], Q._magnitude(aw.q_bits[ok], case.positions[ok],
+                                                          case.cos_sin, eps, norm))
