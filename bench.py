@@ -273,6 +273,8 @@ def device_info() -> dict:
     clock is not the HBM3E data rate."""
     import ctypes
 
+    import torch
+
     props = torch.cuda.get_device_properties(torch.cuda.current_device())
     info = {"name": props.name, "arch": props.gcnArchName,
             "total_memory_GiB": round(props.total_memory / 2 ** 30, 1)}

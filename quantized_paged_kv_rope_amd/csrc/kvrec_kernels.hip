@@ -353,20 +353,26 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
       // intermediate finite; the residuals stay exact down to quotients of
       // 2^-11, below which every result encodes as a signed zero. The sign
       // is restored at the end for the zero quotients of -0 and tiny a.
+      // Clamps are one v_med3_f32 each: inputs are finite (a precondition)
+      // and s is positive and finite, so no operand is NaN. The +-448 clamp
+      // is needed: with a unit scale the conversion rounds values up to 464
+      // to 448 but writes the NaN code (0x7F / 0xFF) above that (measured on
+      // MI355X), where the cache saturates.
       const float rc = __fdiv_rn(1.0f, s);
       const float lim = 1024.0f * s;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float a = fminf(fmaxf(f[k], -lim), lim);
+        const float a = __builtin_amdgcn_fmed3f(f[k], -lim, lim);
         float q = a * rc;
         q = fmaf(fmaf(-s, q, a), rc, q);
         q = fmaf(fmaf(-s, q, a), rc, q);
-        y[k] = fminf(fmaxf(copysignf(q, f[k]), -448.0f), 448.0f);
+        y[k] = __builtin_amdgcn_fmed3f(copysignf(q, f[k]), -448.0f, 448.0f);
       }
     } else {
+      // An infinite quotient (tiny s) clamps to +-448 like any other.
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        y[k] = fminf(fmaxf(__fdiv_rn(f[k], s), -448.0f), 448.0f);
+        y[k] = __builtin_amdgcn_fmed3f(__fdiv_rn(f[k], s), -448.0f, 448.0f);
     }
     st<nt_data>(reinterpret_cast<u32x2 *>(page + off * 512u + lane * 8), encode_e4m3x8(y, 127u));
     return;
