@@ -204,9 +204,10 @@ struct RowInput {
   int32_t cv[E];
 };
 
-// Issues one row's loads. Positions past L read candidate K-1 (a valid
-// address) and are dropped later; offsets are 32-bit bytes from the row's
-// base (K <= 1024).
+// Issues one row's loads. Positions past L (only when E == 1: for E > 1,
+// L = K * RATIO is exactly 64 * E, K being a power of two) read candidate
+// K-1, a valid address, and are dropped later; offsets are 32-bit bytes from
+// the row's base (K <= 1024).
 template <int E>
 __device__ __forceinline__ void load_row(RowInput<E> &in, const int32_t *cand, int64_t cand_stride,
                                          const int32_t *row_ks, int64_t ks_stride,
@@ -217,7 +218,8 @@ __device__ __forceinline__ void load_row(RowInput<E> &in, const int32_t *cand, i
   const char *crow = reinterpret_cast<const char *>(cand + row * cand_stride);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const uint32_t idx = static_cast<uint32_t>(min(lane * E + e, L - 1)) >> split;
+    const int32_t i = lane * E + e;
+    const uint32_t idx = static_cast<uint32_t>(E > 1 ? i : min(i, L - 1)) >> split;
     in.cv[e] = *reinterpret_cast<const int32_t *>(crow + idx * 4u);
   }
 }
@@ -246,7 +248,7 @@ __device__ __forceinline__ void expand_row(const RowInput<E> &in, uint32_t row, 
     const int32_t i = lane * E + e;
     const uint32_t cu = static_cast<uint32_t>(in.cv[e]);
     const uint32_t block = (cu << split) | (static_cast<uint32_t>(i) & split);
-    const bool keep = i < L && cu < max_block && block < max_block;
+    const bool keep = (E > 1 || i < L) && cu < max_block && block < max_block;
     a[e] = keep ? static_cast<int32_t>(block) : kSentinel;
     n_valid += __builtin_popcountll(__builtin_amdgcn_ballot_w64(keep));  // uniform
   }
@@ -274,14 +276,17 @@ __device__ __forceinline__ void expand_row(const RowInput<E> &in, uint32_t row, 
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int32_t i = lane * E + e;
-    if (i < L)
+    if (E > 1 || i < L)
       *reinterpret_cast<int32_t *>(out + static_cast<uint32_t>(i) * 4u) =
           i < n_valid ? a[e] + base : pad;
   }
   if (lane == 0) {
-    const int64_t last_start = static_cast<int64_t>(last) * sbk + ks;
-    const int64_t fill = min(max(ke - last_start, int64_t{1}), static_cast<int64_t>(sbk));
-    end[row * end_stride] = n_valid > 0 ? (n_valid - 1) * sbk + static_cast<int32_t>(fill) : 0;
+    // The last kept block starts at ks + last * SBK < ke (last < max_block),
+    // so the tokens it covers are min(kv_len - last * SBK, SBK) >= 1, in
+    // 32-bit arithmetic: last * SBK < kv_len < 2^31.
+    const uint32_t rest = kv_len - static_cast<uint32_t>(last) * static_cast<uint32_t>(sbk);
+    const int32_t fill = static_cast<int32_t>(min(rest, static_cast<uint32_t>(sbk)));
+    end[row * end_stride] = n_valid > 0 ? (n_valid - 1) * sbk + fill : 0;
   }
 }
 
