@@ -151,6 +151,16 @@ __device__ __forceinline__ uint32_t wave_exclusive_sum(uint32_t v, int lane, uin
   return s + before - v;
 }
 
+// Orders one wave's LDS accesses across this point: every lane's earlier
+// accesses complete before any later one starts (the workgroup-scope fence
+// waits for them) and the compiler moves none across it. The waves of a
+// block never wait for each other: each owns its row and its share of LDS.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // Rank sort of the kept keys of one row into ascending order (positions
 // 0 .. n_valid-1 of a[]), for keys in [0, 32 * words) with words <= kRankWords.
 // Returns false, leaving a[] as it was, when a key repeats.
@@ -164,11 +174,11 @@ __device__ __forceinline__ bool rank_sort(int32_t (&a)[E], int lane, uint32_t wo
   uint2 *mine = bitmap + lane * q;
 #pragma unroll 1
   for (uint32_t j = 0; j < q; ++j) mine[j].x = 0;
-  __syncthreads();
+  wave_lds_sync();
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (a[e] != kSentinel) atomicOr(&bitmap[a[e] >> 5].x, 1u << (a[e] & 31));
-  __syncthreads();
+  wave_lds_sync();
   uint32_t count = 0;
 #pragma unroll 1
   for (uint32_t j = 0; j < q; ++j) count += __builtin_popcount(mine[j].x);
@@ -181,7 +191,7 @@ __device__ __forceinline__ bool rank_sort(int32_t (&a)[E], int lane, uint32_t wo
     mine[j].y = below;
     below += __builtin_popcount(w);
   }
-  __syncthreads();
+  wave_lds_sync();
   // Rank = kept blocks in earlier words + set bits below the key in its word.
 #pragma unroll
   for (int e = 0; e < E; ++e)
@@ -190,7 +200,7 @@ __device__ __forceinline__ bool rank_sort(int32_t (&a)[E], int lane, uint32_t wo
       const uint32_t rank = wp.y + __builtin_popcount(wp.x & ((1u << (a[e] & 31)) - 1u));
       sorted[rank] = a[e];
     }
-  __syncthreads();
+  wave_lds_sync();
   // Positions n_valid and above are never read from a[] afterwards.
 #pragma unroll
   for (int e = 0; e < E; ++e) a[e] = sorted[lane * E + e];
@@ -291,39 +301,32 @@ __device__ __forceinline__ void expand_row(const RowInput<E> &in, uint32_t row, 
 }
 
 
-// R rows per wave (rows first .. first+R-1): every row's loads are issued
-// before the first row is processed, so the later rows' memory latency
-// overlaps the earlier rows' work.
-template <int E, int R>
-__global__ __launch_bounds__(kWave) void expand_kernel(
+// W waves per block, one row each; each wave has its own LDS share.
+template <int E, int W>
+__global__ __launch_bounds__(W * kWave) void expand_kernel(
     const int32_t *cand, int64_t cand_stride, const int32_t *row_ks, int64_t ks_stride,
     const int32_t *row_ke, int64_t ke_stride, uint32_t rows, int32_t num_candidates,
     int32_t ratio, int32_t sbk, int32_t *sparse, int64_t sparse_stride, int32_t *end,
     int64_t end_stride) {
-  const uint32_t first = blockIdx.x * R;
-  if (first >= rows) return;
-  const int lane = threadIdx.x;
+  __shared__ uint2 bitmap[W][kRankWords];
+  __shared__ __align__(16) int32_t sorted[W][kWave * E];
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t row = blockIdx.x * W + wave;
+  if (row >= rows) return;
   const int32_t L = num_candidates * ratio;
   const uint32_t split = static_cast<uint32_t>(ratio) - 1u;  // 1 when each candidate is 2 blocks
-  __shared__ uint2 bitmap[kRankWords];
-  __shared__ __align__(16) int32_t sorted[kWave * E];
-  RowInput<E> in[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (r == 0 || first + r < rows)
-      load_row<E>(in[r], cand, cand_stride, row_ks, ks_stride, row_ke, ke_stride, first + r, lane,
-                  L, split);
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (r == 0 || first + r < rows)
-      expand_row<E>(in[r], first + r, lane, L, split, sbk, sparse, sparse_stride, end, end_stride,
-                    bitmap, sorted);
+  RowInput<E> in;
+  load_row<E>(in, cand, cand_stride, row_ks, ks_stride, row_ke, ke_stride, row, lane, L, split);
+  expand_row<E>(in, row, lane, L, split, sbk, sparse, sparse_stride, end, end_stride,
+                bitmap[wave], sorted[wave]);
 }
 
-// Rows per wave. Measured on MI355X at 16384 rows of 256 blocks: two rows
-// per wave took 11.2 us against 9.9 us for one (the rows' work serialises
-// in the wave; the second row's hidden load latency does not pay for it).
-constexpr int kExpandRows = 1;
+// Waves (rows) per block. Measured on MI355X at 16384 rows of 256 blocks:
+// 1, 2 and 4 waves per block took 8.58, 8.43 and 8.45 us; two rows per wave,
+// one after the other, took 11.2 us against 9.9 us for one (the rows' work
+// serialises in the wave).
+constexpr int kExpandWaves = 2;
 
 template <int E>
 hipError_t launch_expand_e(const ExpandArgs &x, hipStream_t stream) {
@@ -335,9 +338,9 @@ hipError_t launch_expand_e(const ExpandArgs &x, hipStream_t stream) {
   int32_t *sparse = x.sparse, *end = x.end;
   void *params[] = {&cand, &cs,    &ks,  &kss,    &ke, &kes,    &rows,
                     &k,    &ratio, &sbk, &sparse, &ss, &end,    &es};
-  const uint32_t waves = (rows + kExpandRows - 1) / kExpandRows;
-  return hipLaunchKernel(reinterpret_cast<const void *>(expand_kernel<E, kExpandRows>),
-                         dim3(waves), dim3(kWave), params, 0, stream);
+  const uint32_t blocks = (rows + kExpandWaves - 1) / kExpandWaves;
+  return hipLaunchKernel(reinterpret_cast<const void *>(expand_kernel<E, kExpandWaves>),
+                         dim3(blocks), dim3(kExpandWaves * kWave), params, 0, stream);
 }
 
 }  // namespace
