@@ -164,7 +164,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Rank sort of the kept keys of one row into ascending order (positions
 // 0 .. n_valid-1 of a[]), for keys in [0, 32 * words) with words <= kRankWords.
 // Returns false, leaving a[] as it was, when a key repeats.
-template <int E>
+//
+// kPairs (RATIO 2, E >= 2): a[2m] and a[2m+1] are the blocks 2c and 2c + 1 of
+// one candidate c. They share a bitmap word, and 2c + 1 is kept only when 2c
+// is, so one update sets both bits and rank(2c + 1) = rank(2c) + 1.
+template <int E, bool kPairs>
 __device__ __forceinline__ bool rank_sort(int32_t (&a)[E], int lane, uint32_t words,
                                           int32_t n_valid, uint2 *bitmap, int32_t *sorted) {
   // Words [0, 64 q) are used, lane l owning l*q .. l*q + q-1; those past
@@ -175,9 +179,16 @@ __device__ __forceinline__ bool rank_sort(int32_t (&a)[E], int lane, uint32_t wo
 #pragma unroll 1
   for (uint32_t j = 0; j < q; ++j) mine[j].x = 0;
   wave_lds_sync();
+  if constexpr (kPairs) {
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (a[e] != kSentinel) atomicOr(&bitmap[a[e] >> 5].x, 1u << (a[e] & 31));
+    for (int e = 0; e < E; e += 2)
+      if (a[e] != kSentinel)
+        atomicOr(&bitmap[a[e] >> 5].x, (a[e + 1] != kSentinel ? 3u : 1u) << (a[e] & 31));
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (a[e] != kSentinel) atomicOr(&bitmap[a[e] >> 5].x, 1u << (a[e] & 31));
+  }
   wave_lds_sync();
   uint32_t count = 0;
 #pragma unroll 1
@@ -194,11 +205,13 @@ __device__ __forceinline__ bool rank_sort(int32_t (&a)[E], int lane, uint32_t wo
   wave_lds_sync();
   // Rank = kept blocks in earlier words + set bits below the key in its word.
 #pragma unroll
-  for (int e = 0; e < E; ++e)
+  for (int e = 0; e < E; e += (kPairs ? 2 : 1))
     if (a[e] != kSentinel) {
       const uint2 wp = bitmap[a[e] >> 5];
       const uint32_t rank = wp.y + __builtin_popcount(wp.x & ((1u << (a[e] & 31)) - 1u));
       sorted[rank] = a[e];
+      if constexpr (kPairs)
+        if (a[e + 1] != kSentinel) sorted[rank + 1] = a[e + 1];
     }
   wave_lds_sync();
   // Positions n_valid and above are never read from a[] afterwards.
@@ -264,8 +277,15 @@ __device__ __forceinline__ void expand_row(const RowInput<E> &in, uint32_t row, 
   }
 
   bool done = false;
-  if (max_block <= kRankMaxBlocks)  // uniform
-    done = rank_sort<E>(a, lane, (max_block + 31u) / 32u, n_valid, bitmap, sorted);
+  if (max_block <= kRankMaxBlocks) {  // uniform
+    const uint32_t words = (max_block + 31u) / 32u;
+    if constexpr (E >= 2) {
+      done = split != 0u ? rank_sort<E, true>(a, lane, words, n_valid, bitmap, sorted)
+                         : rank_sort<E, false>(a, lane, words, n_valid, bitmap, sorted);
+    } else {
+      done = rank_sort<E, false>(a, lane, words, n_valid, bitmap, sorted);
+    }
+  }
   if (!done) {
     // Bitonic sort of the 64 * E keys, ascending.
     const int32_t addr_xor32 = (lane ^ 32) << 2;
