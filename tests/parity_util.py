@@ -19,7 +19,7 @@ from quantized_paged_kv_rope_amd import workloads as W
 
 
 def workers() -> int:
-    # at most 16: the CPU share of a one-GPU machine
+    # at most 16 worker threads: the host CPU share of a one-GPU machine
     return max(1, min(16, os.cpu_count() or 1))
 
 
