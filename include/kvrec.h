@@ -189,8 +189,9 @@ typedef struct kvrec_insert_options {
 /* kvrec_insert with options (NULL = the defaults). Same arguments, layout
  * and errors as kvrec_insert, plus KVREC_ERR_OPTION for an option out of
  * range. With rope == KVREC_ROPE_NONE the table is not read and
- * cos_sin_cache may be NULL; with compress_ratio == 1 as well, positions are
- * not read either and may be NULL (max_pos is then ignored). */
+ * cos_sin_cache may be NULL (nor is it checked); with compress_ratio == 1 as
+ * well, positions are not read either, may be NULL, and skip no token even
+ * when given and out of range (positions and max_pos are then ignored). */
 int kvrec_insert_ex(const void *kv, int64_t num_tokens, const kvrec_cache *k_cache,
                     const int64_t *slot_mapping, const int64_t *positions,
                     const float *cos_sin_cache, int64_t max_pos, int32_t block_size,

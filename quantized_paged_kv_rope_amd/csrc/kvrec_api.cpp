@@ -121,16 +121,19 @@ int kvrec_insert_ex(const void *kv, int64_t num_tokens, const kvrec_cache *k_cac
   if (opt.sanitize_nans != 0 && opt.sanitize_nans != 1) return KVREC_ERR_OPTION;
   if (num_tokens < 0 || num_tokens > kMaxCount) return KVREC_ERR_SIZE;
   if (num_tokens == 0) return KVREC_OK;
-  // Positions are read for the rotation and the ratio gate; the table only
-  // for the rotation.
+  // Positions are read for the rotation and the ratio gate, the table only
+  // for the rotation; what is not read is neither checked nor passed on
+  // (the rotation-free insert with ratio 1 ignores positions and max_pos).
   const bool needs_positions = opt.rope != KVREC_ROPE_NONE || opt.compress_ratio != 1;
   const bool needs_table = opt.rope != KVREC_ROPE_NONE;
+  const int64_t *pos = needs_positions ? positions : nullptr;
+  const float *table = needs_table ? cos_sin_cache : nullptr;
   if (kv == nullptr || slot_mapping == nullptr) return KVREC_ERR_NULL;
-  if ((needs_positions && positions == nullptr) || (needs_table && cos_sin_cache == nullptr))
+  if ((needs_positions && pos == nullptr) || (needs_table && table == nullptr))
     return KVREC_ERR_NULL;
-  if (positions != nullptr && (max_pos < 1 || max_pos > kMaxPos)) return KVREC_ERR_SIZE;
-  if (misaligned(kv, 16) || misaligned(cos_sin_cache, 16) || misaligned(slot_mapping, 8) ||
-      misaligned(positions, 8))
+  if (pos != nullptr && (max_pos < 1 || max_pos > kMaxPos)) return KVREC_ERR_SIZE;
+  if (misaligned(kv, 16) || misaligned(table, 16) || misaligned(slot_mapping, 8) ||
+      misaligned(pos, 8))
     return KVREC_ERR_ALIGNMENT;
   kvrec::InsertOptions o;
   o.rope = opt.rope;
@@ -138,15 +141,12 @@ int kvrec_insert_ex(const void *kv, int64_t num_tokens, const kvrec_cache *k_cac
   o.ratio = static_cast<uint32_t>(opt.compress_ratio);
   division_magic(o.ratio, &o.ratio_magic, &o.ratio_shift);
   memcpy(&o.amax_floor_bits, &opt.amax_floor, sizeof o.amax_floor_bits);
-  // Without positions (the rotation-free insert with ratio 1) the kernels
-  // skip the position checks; the table is never read without a rotation.
-  const int64_t *pos = needs_positions ? positions : nullptr;
+  // Without positions the kernels skip the position checks.
   if (pos == nullptr) max_pos = 1;
-  if (!needs_table) cos_sin_cache = nullptr;
   const kvrec::Format format =
       record == KVREC_RECORD_LEGACY ? kvrec::Format::kLegacy : kvrec::Format::kMxfp8;
   const hipError_t err =
-      kvrec::launch_insert(kv, num_tokens, g, slot_mapping, pos, cos_sin_cache, max_pos, format, o,
+      kvrec::launch_insert(kv, num_tokens, g, slot_mapping, pos, table, max_pos, format, o,
                            nullptr, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? KVREC_OK : KVREC_ERR_HIP;
 }
