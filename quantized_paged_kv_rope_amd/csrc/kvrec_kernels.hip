@@ -183,7 +183,9 @@ __device__ __forceinline__ uint32_t lane_read(uint32_t v, int src_lane) {
 // eight. C is 512 blocks (chunks of 512 measured 1-2% faster than one
 // contiguous range per XCD for single launches on clean caches: insert 89.7
 // -> 87.5 us, gather 68.4 -> 66.9 us at 262144 tokens; the same back to back;
-// chunks of 4096 made the gather slower, 72 us), or for grids of up to
+// chunks of 4096 made the gather slower, 72 us, and the insert + gather step
+// took 139.5 us with chunks of 512 against 140-142 with 256 or 1024), or for
+// grids of up to
 // 8 * 512 blocks the power of two that gives each XCD one chunk. The grid is
 // padded to whole chunks on every XCD; the padding blocks find no work.
 constexpr int kXcds = 8;
