@@ -5,6 +5,8 @@ oracle's exactly.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -162,3 +164,39 @@ def test_rank_sort_and_network_paths(k, ratio, sbk):
     bad = np.argwhere(got[0] != want[0])
     assert len(bad) == 0, (bad[:5], [MAX_BLOCKS[r // 3] for r in bad[:5, 0]])
     assert np.array_equal(got[1], want[1])
+
+
+EXPAND_CASES = int(os.environ.get("KVREC_RANDOM_EXPAND_CASES", "40"))
+
+
+@pytest.mark.parametrize("seed", range(EXPAND_CASES))
+def test_random_expansion(seed):
+    """Random shapes (K 1..1024, both ratios and block sizes, 1..300 rows),
+    row lengths from tens of tokens to 2^24, distinct or repeating
+    candidates with negative and out-of-range entries: every output against
+    the oracle. KVREC_RANDOM_EXPAND_CASES raises the count."""
+    rng = np.random.default_rng(90000 + seed)
+    k = int(2 ** rng.integers(0, 11))
+    ratio = int(rng.choice([1, 2]))
+    if k * ratio > 1024:
+        k //= 2
+    sbk = int(rng.choice([8, 16]))
+    rows = int(rng.integers(1, 300))
+    lens = rng.integers(0, [64, 40000, 2 ** 24][int(rng.integers(3))], rows)
+    ks = rng.integers(0, 2 ** 31 - 1 - int(lens.max()) - 1, rows)
+    ke = ks + lens - rng.integers(0, 3, rows) * (lens == 0)
+    ks, ke = ks.astype(np.int32), np.maximum(ke, 0).astype(np.int32)
+    cand = np.empty((rows, k), np.int32)
+    for r in range(rows):
+        span = -(-int(max(ke[r] - ks[r], 0)) // (sbk * ratio)) + 8
+        if rng.random() < 0.7:
+            row = rng.choice(span, min(k, span), replace=False) - 2
+            row = np.concatenate([row, np.full(k - len(row), -1)])
+        else:
+            row = rng.integers(-2, span - 2, k)
+        row[rng.random(k) < 0.1] = -1
+        cand[r] = row
+    got = _gpu(cand, ks, ke, ratio, sbk)
+    want = oracle.expand_candidates(cand, ks, ke, ratio, sbk)
+    assert np.array_equal(got[0], want[0]), (seed, np.argwhere(got[0] != want[0])[:5])
+    assert np.array_equal(got[1], want[1]), seed

@@ -6,8 +6,13 @@ out-of-range slots and positions (which the kernels skip, like the oracle),
 the compressed-KV options (rotation, ratio gate, amax floor, NaN sanitising)
 and the fp8 cache's scale. Every byte of the pre-filled cache backing and
 every gathered row is compared with the oracle.
+
+The case counts default to 48 and 24; KVREC_RANDOM_CASES and
+KVREC_RANDOM_QKV_CASES raise them for a longer campaign.
 """
 from __future__ import annotations
+
+import os
 
 import numpy as np
 import pytest
@@ -17,7 +22,7 @@ from tests import parity_util as P
 
 pytestmark = pytest.mark.gpu
 
-CASES = 48
+CASES = int(os.environ.get("KVREC_RANDOM_CASES", "48"))
 ALIGN = {W.RECORD_MXFP8: 512, W.RECORD_LEGACY: 576, W.RECORD_BF16: 16, W.RECORD_FP8: 16}
 
 
@@ -84,7 +89,7 @@ def test_random_configuration(seed):
         assert np.array_equal(out, want_g), (case.name, P.first_diff(out, want_g))
 
 
-QKV_CASES = 24
+QKV_CASES = int(os.environ.get("KVREC_RANDOM_QKV_CASES", "24"))
 
 
 @pytest.mark.parametrize("seed", range(QKV_CASES))
