@@ -360,8 +360,10 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
       // a second (correctly rounded). a is first clamped to +-1024 s: any
       // larger quotient saturates anyway, and the clamp keeps every
       // intermediate finite; the residuals stay exact down to quotients of
-      // 2^-11, below which every result encodes as a signed zero. The sign
-      // is restored at the end for the zero quotients of -0 and tiny a.
+      // 2^-11, below which every result encodes as a signed zero. Each
+      // correction is written q - (s q - a) rc, which rounds exactly like
+      // q + (a - s q) rc (rounding to nearest is symmetric) but keeps the
+      // sign of a zero quotient: -0 / s stays -0 with no separate sign fix.
       // Clamps are one v_med3_f32 each: inputs are finite (a precondition)
       // and s is positive and finite, so no operand is NaN. The +-448 clamp
       // is needed: with a unit scale the conversion rounds values up to 464
@@ -373,9 +375,9 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
       for (int k = 0; k < 8; ++k) {
         const float a = __builtin_amdgcn_fmed3f(f[k], -lim, lim);
         float q = a * rc;
-        q = fmaf(fmaf(-s, q, a), rc, q);
-        q = fmaf(fmaf(-s, q, a), rc, q);
-        y[k] = __builtin_amdgcn_fmed3f(copysignf(q, f[k]), -448.0f, 448.0f);
+        q = fmaf(-fmaf(s, q, -a), rc, q);
+        q = fmaf(-fmaf(s, q, -a), rc, q);
+        y[k] = __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
       }
     } else {
       // An infinite quotient (tiny s) clamps to +-448 like any other.
