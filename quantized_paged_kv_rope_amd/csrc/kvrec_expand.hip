@@ -8,7 +8,9 @@
 // ks / SBK and padded with the last kept block; `end` counts the valid sparse
 // token columns. Integer work only: the result is exact.
 //
-// Shape. One wave64 per row. The L = K * RATIO expanded blocks are held in
+// Shape. One wave64 per row, two waves per block; each wave has its own LDS
+// share and orders only its own LDS accesses, so the two rows of a block may
+// take different paths below. The L = K * RATIO expanded blocks are held in
 // registers, E = max(L, 64) / 64 per lane (lane l holds positions
 // l*E .. l*E + E-1); positions past L and dropped blocks hold a sentinel
 // larger than any kept block. The kept count comes from ballots. Two ways to
@@ -18,9 +20,10 @@
 //   blocks are distinct (the candidates of a top-k are): each kept block sets
 //   its bit in a bitmap in LDS; a prefix sum of the words' popcounts gives
 //   every block its rank, the number of kept blocks below it; each block is
-//   written to its rank in an LDS row and read back in order. The bitmap's
-//   popcount equals the kept count exactly when no block repeats, so a
-//   repeated block sends the row to the network below.
+//   written to its rank in an LDS row and read back in order (with RATIO 2
+//   the two blocks of a candidate share one bitmap update and one rank). The
+//   bitmap's popcount equals the kept count exactly when no block repeats,
+//   so a repeated block sends the row to the network below.
 // - A bitonic network otherwise: exchanges at distance < E stay inside a
 //   lane; the others read the partner lane by DPP (lane distances 1..8),
 //   ds_swizzle (16) or ds_bpermute (32), and keep the smaller or larger key
