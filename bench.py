@@ -15,8 +15,9 @@ a bounded sample of the same workload.
 
 The JSON line on stdout is the only headline. --all-configs also times each
 kernel on the other workloads (single launches after a 1 GiB read that
-leaves the caches clean, and back-to-back launches replayed from a HIP graph)
-and prints them as a table on stderr.
+leaves the caches clean, and back-to-back launches replayed from a HIP graph),
+prints them as a table on stderr and adds them to the JSON line as
+"all_configs".
 """
 from __future__ import annotations
 
@@ -424,7 +425,9 @@ def main() -> int:
     if args.all_configs:
         del kv, slots, pos, cos_sin, idx, backing, k_cache, out
         torch.cuda.empty_cache()
-        all_configs_report(dev)
+        result["all_configs"] = [
+            {k: (v.item() if isinstance(v, np.generic) else v) for k, v in row.items()}
+            for row in all_configs_report(dev)]
     print(json.dumps(result), flush=True)
     return 0
 
