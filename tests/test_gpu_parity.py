@@ -426,3 +426,42 @@ def test_largest_page(record):
     assert np.array_equal(out, want_out), P.first_diff(out, want_out)
     del backing, kc
     torch.cuda.empty_cache()
+
+
+def test_concurrent_calls_on_two_streams():
+    """The library keeps no state: two host threads, each with its own
+    stream (default priority) and cache, insert and gather at the same time
+    (ctypes releases the interpreter lock around each call); both caches
+    and both gathers equal the oracle's."""
+    import threading
+
+    cases = [W.custom_insert(3100 + i, 3000, rec, 64, 60, max_pos=4096)
+             for i, rec in enumerate((528, 584))]
+    devs = [P.DeviceCase(c) for c in cases]
+    streams = [torch.cuda.Stream() for _ in cases]
+    outs = [None, None]
+    errors = []
+
+    def work(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(20):
+                    devs[i].insert()
+                    outs[i] = B.kvrec_gather(devs[i].k_cache, P.dev(cases[i].gather_indices))
+            streams[i].synchronize()
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for c, d, o in zip(cases, devs, outs):
+        want = P.oracle_insert(c, c.initial_backing())
+        got = d.backing_host()
+        assert np.array_equal(got, want), (c.record, P.first_diff(got, want))
+        want_g = P.oracle_gather(c, want, c.gather_indices)
+        assert np.array_equal(P.host_bits(o), want_g), c.record
