@@ -283,8 +283,11 @@ def test_rope_exact_tables_pin_pairing_and_signs():
     Distinct c and s per column detect a swapped cos/sin half, a wrong pair
     partner, or a wrong sign."""
     n, P = 256, 5
-    x = RNG.standard_normal((n, 512)).astype(np.float32)
-    kv = _torch_bf16(np.clip(x, -4, 4))
+    # k / 64 with |k| <= 255: at most 8 significant bits (exact in bf16) and
+    # a bounded exponent range, so x * c (c = j / 8) is an integer multiple of
+    # 2^-9 below 2^12 and so is the sum of two such products: all exact in fp32.
+    x = (RNG.integers(-255, 256, (n, 512)) / 64.0).astype(np.float32)
+    kv = _torch_bf16(x)
     xf = _bf16_to_f32(kv).astype(np.float64)
     table = np.zeros((P, 64), np.float32)
     table[:, :32] = RNG.integers(-8, 9, (P, 32)) / 8.0
