@@ -260,7 +260,10 @@ int kvrec_qnorm_rope_insert(const void *q_in, void *q_out, int32_t num_heads, fl
  *     kept ones with the last kept block + base (base when none is kept);
  *   - end = (n_valid - 1) * SBK + min(max(ke - (last * SBK + ks), 1), SBK),
  *     or 0 when nothing is kept (only the last block can be partial).
- * Integer arithmetic is exact (no int32 wrap of intermediate values).
+ * Integer arithmetic is exact (no int32 wrap of intermediate values). For
+ * rows with ke - ks > 2^31 - SBK this differs from the page's int32 program,
+ * whose ke - ks + SBK - 1 wraps negative there so that it keeps no block:
+ * here such a row keeps the blocks that cover [ks, ke), as any shorter row.
  *
  *   candidate_blocks (device) int32, row r at r * cand_stride (elements),
  *                    K entries; cand_stride >= K.

@@ -487,7 +487,10 @@ int orc_gather(const uint8_t *cache, int64_t num_blocks, int64_t page_stride,
 /* K * RATIO (the store covers every expanded position); ks >= 0 and ke >= 0 */
 /* (so the page's integer division is plain); intermediate values (2c + 1,   */
 /* ke - ks + SBK - 1, last * SBK + ks) are exact integers, not wrapped to    */
-/* int32 (every stored result fits in int32).                                */
+/* int32 (every stored result fits in int32). This changes results from the  */
+/* page's int32 program for rows with ke - ks > 2^31 - SBK only: there its   */
+/* ke - ks + SBK - 1 wraps negative and it keeps no block, while this keeps  */
+/* the blocks that cover [ks, ke).                                           */
 /* ------------------------------------------------------------------------ */
 static int compare_int32(const void *a, const void *b) {
   int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;

@@ -117,3 +117,46 @@ def test_rejects_bad_parameters():
     for ratio, sbk in ((3, 8), (0, 8), (1, 0)):
         with pytest.raises(ValueError):
             oracle.expand_candidates(cand, i32(0), i32(10), ratio, sbk)
+
+
+def test_rows_at_the_int32_edge():
+    """Rows whose range length ke - ks sits at 2^31 - SBK - 1, 2^31 - SBK and
+    2^31 - SBK + 1, against hand-worked values. The page's kernel forms
+    ke - ks + SBK - 1 in int32; past 2^31 - SBK that sum wraps negative and
+    its program keeps no block (all outputs 0, end 0). The expansion here
+    takes the range's blocks in exact integers, so those rows keep the
+    blocks that cover [ks, ke), as they do below the edge.
+
+    SBK 16, RATIO 1, ks 0, candidates (2^27 - 1, 7, 2^27 - 2, -1):
+      ke = 2^31 - 17: max_block = ceil(ke / 16) = 2^27 - 1, so 7 and 2^27 - 2
+        are kept; the last starts at token (2^27 - 2) * 16 = 2^31 - 32 and
+        holds ke - (2^31 - 32) = 15 tokens of the range: end = 16 + 15 = 31.
+      ke = 2^31 - 16: the same blocks; the last block is full: end = 32.
+      ke = 2^31 - 15: max_block = 2^27, so 2^27 - 1 is kept too; it starts at
+        2^31 - 16 and holds 1 token: end = 2 * 16 + 1 = 33.
+    SBK 8, RATIO 2 (candidate c -> sparse blocks 2c, 2c + 1), ks 0,
+    candidates (2^27 - 1, 3, -1, 2^27 + 5):
+      ke = 2^31 - 8: max_block = 2^28 - 1; kept 6, 7, 2^28 - 2; the last
+        starts at 2^31 - 16 and holds 8 tokens: end = 2 * 8 + 8 = 24.
+      ke = 2^31 - 7: max_block = 2^28; 2^28 - 1 is kept too, starting at
+        2^31 - 8 with 1 token: end = 3 * 8 + 1 = 25.
+    """
+    b27, b28 = 2 ** 27, 2 ** 28
+    cand = np.array([[b27 - 1, 7, b27 - 2, -1]] * 3, np.int32)
+    ke = i32(2 ** 31 - 17, 2 ** 31 - 16, 2 ** 31 - 15)
+    sparse, end = oracle.expand_candidates(cand, i32(0, 0, 0), ke, 1, 16)
+    assert sparse.tolist() == [[7, b27 - 2, b27 - 2, b27 - 2],
+                               [7, b27 - 2, b27 - 2, b27 - 2],
+                               [7, b27 - 2, b27 - 1, b27 - 1]]
+    assert end.tolist() == [31, 32, 33]
+    for r in range(3):
+        _check_row(cand[r].tolist(), 0, int(ke[r]), 1, 16, sparse[r], int(end[r]))
+
+    cand = np.array([[b27 - 1, 3, -1, b27 + 5]] * 2, np.int32)
+    ke = i32(2 ** 31 - 8, 2 ** 31 - 7)
+    sparse, end = oracle.expand_candidates(cand, i32(0, 0), ke, 2, 8)
+    assert sparse.tolist() == [[6, 7, b28 - 2] + [b28 - 2] * 5,
+                               [6, 7, b28 - 2, b28 - 1] + [b28 - 1] * 4]
+    assert end.tolist() == [24, 25]
+    for r in range(2):
+        _check_row(cand[r].tolist(), 0, int(ke[r]), 2, 8, sparse[r], int(end[r]))
