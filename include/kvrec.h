@@ -33,10 +33,16 @@
  *   - Every argument check runs on the host before any launch; on error the
  *     call returns a negative kvrec_status and nothing is launched or
  *     written. The library never throws or aborts across this ABI.
+ *   - A call over more than 2^21 waves of work (2^21 tokens of an insert,
+ *     2^22 gather rows, 2^21 expansion rows, fewer attention-write tokens)
+ *     runs as several kernel launches on `stream`, one per consecutive slice
+ *     of the rows, in order. If a later launch fails (KVREC_ERR_HIP), the
+ *     slices before it have been enqueued.
  *   - Device-resident values are not inspected on the host. Preconditions
  *     the caller keeps: non-negative slots distinct within one insert; kv
- *     finite with |x| < 2^127 (so the rotation cannot overflow); kv, out and
- *     token_indices do not overlap the cache. As a memory-safety guard the
+ *     finite with |x| < 2^127 (so the rotation cannot overflow), except
+ *     that NaN (never an infinity) is allowed in kvrec_insert_ex with
+ *     sanitize_nans = 1; kv, out and token_indices do not overlap the cache. As a memory-safety guard the
  *     kernels skip a token whose slot is >= num_blocks * block_size or whose
  *     position is outside [0, max_pos), and gather a zero row for an index
  *     >= num_blocks * block_size.
@@ -172,7 +178,8 @@ int kvrec_insert(const void *kv, int64_t num_tokens, const kvrec_cache *k_cache,
  *                   are written, rotated with table row position / R * R.
  *   amax_floor      finite, >= 0: each group's amax is raised to it before
  *                   the exponent is chosen (the excerpt uses 1e-4; 0 = none).
- *   sanitize_nans   0 or 1: rotated NaNs become +0 before quantisation. */
+ *   sanitize_nans   0 or 1: rotated NaNs become +0 before quantisation;
+ *                   with 1, kv may hold NaNs (never infinities). */
 typedef enum kvrec_rope {
   KVREC_ROPE_NEOX = 0,
   KVREC_ROPE_INTERLEAVED = 1,

@@ -1,5 +1,6 @@
 // kvrec_api.cpp - the C ABI declared in include/kvrec.h: argument checks on
-// the host, then one kernel launch on the caller's stream.
+// the host, then the kernel launch (one per slice of at most 2^21 waves) on
+// the caller's stream.
 //
 // Checks follow the validation list of the page's KV-only op ([KV-only op]
 // 实现拆解 1: dtype/shape/stride/record-width checks at the op's entry, and
@@ -20,7 +21,9 @@
 
 namespace {
 
-constexpr int64_t kMaxCount = int64_t{1} << 30;  // rows and slots; keeps grids < 2^31 blocks
+// Rows and slots per call: indices stay 32-bit on the device. Calls of more
+// rows than one launch takes run as several launches (kvrec::kMaxLaunchWaves).
+constexpr int64_t kMaxCount = int64_t{1} << 30;
 constexpr int64_t kMaxPos = int64_t{1} << 30;    // cos/sin rows (a 256 GB table); pos + 1 < 2^31
 constexpr int32_t kMaxHeads = 1024;              // q heads of the attention write
 constexpr int32_t kMaxExpanded = 1024;           // K * RATIO of the candidate expansion

@@ -368,14 +368,27 @@ hipError_t launch_expand_e(const ExpandArgs &x, hipStream_t stream) {
 
 }  // namespace
 
+// One wave per row; more rows than one launch takes run as several launches
+// over consecutive row slices.
 hipError_t launch_expand(const ExpandArgs &x, hipStream_t stream) {
   const int64_t L = static_cast<int64_t>(x.num_candidates) * x.ratio;
-  if (L <= 64) return launch_expand_e<1>(x, stream);
-  if (L <= 128) return launch_expand_e<2>(x, stream);
-  if (L <= 256) return launch_expand_e<4>(x, stream);
-  if (L <= 512) return launch_expand_e<8>(x, stream);
-  if (L <= 1024) return launch_expand_e<16>(x, stream);
-  return hipErrorInvalidValue;
+  for (int64_t s = 0; s < x.rows; s += kMaxLaunchWaves) {
+    ExpandArgs y = x;
+    y.rows = x.rows - s < kMaxLaunchWaves ? x.rows - s : kMaxLaunchWaves;
+    y.cand = x.cand + s * x.cand_stride;
+    y.ks = x.ks + s * x.ks_stride;
+    y.ke = x.ke + s * x.ke_stride;
+    y.sparse = x.sparse + s * x.sparse_stride;
+    y.end = x.end + s * x.end_stride;
+    const hipError_t err = L <= 64    ? launch_expand_e<1>(y, stream)
+                           : L <= 128 ? launch_expand_e<2>(y, stream)
+                           : L <= 256 ? launch_expand_e<4>(y, stream)
+                           : L <= 512 ? launch_expand_e<8>(y, stream)
+                           : L <= 1024 ? launch_expand_e<16>(y, stream)
+                                       : hipErrorInvalidValue;
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kvrec

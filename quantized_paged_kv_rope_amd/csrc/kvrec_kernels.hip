@@ -832,10 +832,22 @@ dim3 xcd_grid(int64_t waves, uint32_t *xcd_shift) {
   return dim3(static_cast<uint32_t>(chunks * chunk * kXcds));
 }
 
+// Runs launch(first_row, rows) over consecutive slices of at most `slice`
+// rows, stopping at the first launch error.
+template <typename F>
+hipError_t sliced(int64_t n, int64_t slice, F launch) {
+  for (int64_t s = 0; s < n; s += slice) {
+    const hipError_t err = launch(s, n - s < slice ? n - s : slice);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
 template <int P, int W, int T, int kFmt, int kRope, bool kSanitize, bool kOptions>
-hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
-                         const int64_t *positions, const float *cos_sin, int64_t max_pos,
-                         const InsertOptions &o, const float *fp8_scale, hipStream_t stream) {
+hipError_t launch_insert_slice(const void *kv, int64_t n, const CacheGeom &g,
+                               const int64_t *slots, const int64_t *positions,
+                               const float *cos_sin, int64_t max_pos, const InsertOptions &o,
+                               const float *fp8_scale, hipStream_t stream) {
   uint32_t xcd_shift = 0;
   const dim3 grid = xcd_grid<W>((n + T - 1) / T, &xcd_shift);
   uint32_t n32 = static_cast<uint32_t>(n), mp = static_cast<uint32_t>(max_pos);
@@ -854,6 +866,17 @@ hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const in
       dim3(W * kWave), params, 0, stream);
 }
 
+template <int P, int W, int T, int kFmt, int kRope, bool kSanitize, bool kOptions>
+hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const int64_t *slots,
+                         const int64_t *positions, const float *cos_sin, int64_t max_pos,
+                         const InsertOptions &o, const float *fp8_scale, hipStream_t stream) {
+  return sliced(n, kMaxLaunchWaves * T, [&](int64_t s, int64_t m) {
+    return launch_insert_slice<P, W, T, kFmt, kRope, kSanitize, kOptions>(
+        static_cast<const u32x4 *>(kv) + s * kWave, m, g, slots + s,
+        positions != nullptr ? positions + s : nullptr, cos_sin, max_pos, o, fp8_scale, stream);
+  });
+}
+
 // Tokens per wave of the gated insert (ratio R > 1): about two kept tokens
 // per group, i.e. one round of loads per wave (measured on MI355X at the
 // 262144-token prefill shape: groups of R, 2R, 4R and 8R tokens took 33.6,
@@ -861,10 +884,11 @@ hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const in
 uint32_t gated_group(uint32_t ratio) { return ratio >= 32 ? 64u : 2u * ratio; }
 
 template <int kFmt, int kRope, bool kSanitize, bool kOptions, bool kGate>
-hipError_t launch_insert_group(const void *kv, int64_t n, const CacheGeom &g,
-                               const int64_t *slots, const int64_t *positions,
-                               const float *cos_sin, int64_t max_pos, const InsertOptions &o,
-                               uint32_t group, const float *fp8_scale, hipStream_t stream) {
+hipError_t launch_insert_group_slice(const void *kv, int64_t n, const CacheGeom &g,
+                                     const int64_t *slots, const int64_t *positions,
+                                     const float *cos_sin, int64_t max_pos,
+                                     const InsertOptions &o, uint32_t group,
+                                     const float *fp8_scale, hipStream_t stream) {
   uint32_t xcd_shift = 0;
   const dim3 grid = xcd_grid<1>((n + group - 1) / group, &xcd_shift);
   uint32_t n32 = static_cast<uint32_t>(n), mp = static_cast<uint32_t>(max_pos);
@@ -884,6 +908,18 @@ hipError_t launch_insert_group(const void *kv, int64_t n, const CacheGeom &g,
       grid, dim3(kWave), params, 0, stream);
 }
 
+template <int kFmt, int kRope, bool kSanitize, bool kOptions, bool kGate>
+hipError_t launch_insert_group(const void *kv, int64_t n, const CacheGeom &g,
+                               const int64_t *slots, const int64_t *positions,
+                               const float *cos_sin, int64_t max_pos, const InsertOptions &o,
+                               uint32_t group, const float *fp8_scale, hipStream_t stream) {
+  return sliced(n, kMaxLaunchWaves * group, [&](int64_t s, int64_t m) {
+    return launch_insert_group_slice<kFmt, kRope, kSanitize, kOptions, kGate>(
+        static_cast<const u32x4 *>(kv) + s * kWave, m, g, slots + s, positions + s, cos_sin,
+        max_pos, o, group, fp8_scale, stream);
+  });
+}
+
 template <int kFmt, int kRope, bool kSanitize, bool kOptions = true>
 hipError_t launch_insert_tuned(const void *kv, int64_t n, const CacheGeom &g,
                                const int64_t *slots, const int64_t *positions,
@@ -895,8 +931,8 @@ hipError_t launch_insert_tuned(const void *kv, int64_t n, const CacheGeom &g,
 }
 
 template <bool kLegacy, int R, int P, int W>
-hipError_t launch_gather(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
-                         hipStream_t stream) {
+hipError_t launch_gather_slice(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
+                               hipStream_t stream) {
   uint32_t xcd_shift = 0;
   const dim3 grid = xcd_grid<W>((n + R - 1) / R, &xcd_shift);
   uint32_t n32 = static_cast<uint32_t>(n);
@@ -909,10 +945,19 @@ hipError_t launch_gather(const CacheGeom &g, const int32_t *indices, int64_t n, 
                          dim3(W * kWave), params, 0, stream);
 }
 
+template <bool kLegacy, int R, int P, int W>
+hipError_t launch_gather(const CacheGeom &g, const int32_t *indices, int64_t n, void *out,
+                         hipStream_t stream) {
+  return sliced(n, kMaxLaunchWaves * R, [&](int64_t s, int64_t m) {
+    return launch_gather_slice<kLegacy, R, P, W>(g, indices + s, m,
+                                                 static_cast<u32x4 *>(out) + s * kWave, stream);
+  });
+}
+
 template <int kFmt, bool kNorm>
-hipError_t launch_qkv_t(const QArgs &q, const void *kv, int64_t n, const CacheGeom &g,
-                        const int64_t *slots, const int64_t *positions, const float *cos_sin,
-                        int64_t max_pos, hipStream_t stream) {
+hipError_t launch_qkv_slice(const QArgs &q, const void *kv, int64_t n, const CacheGeom &g,
+                            const int64_t *slots, const int64_t *positions, const float *cos_sin,
+                            int64_t max_pos, hipStream_t stream) {
   uint32_t wpt = static_cast<uint32_t>((q.heads + kQHeadsPerWave - 1) / kQHeadsPerWave);
   uint32_t q_waves = static_cast<uint32_t>(n) * wpt;
   uint32_t xcd_shift = 0;
@@ -936,6 +981,22 @@ hipError_t launch_qkv_t(const QArgs &q, const void *kv, int64_t n, const CacheGe
       reinterpret_cast<const void *>(
           qkv_kernel<insert_policy<kFmt>(), kFmt, kQHeadsPerWave, kNorm>),
       grid, dim3(kWave), params, 0, stream);
+}
+
+// ceil(heads / 2) q waves and one insert wave per token.
+template <int kFmt, bool kNorm>
+hipError_t launch_qkv_t(const QArgs &q, const void *kv, int64_t n, const CacheGeom &g,
+                        const int64_t *slots, const int64_t *positions, const float *cos_sin,
+                        int64_t max_pos, hipStream_t stream) {
+  const int64_t waves_per_token = (q.heads + kQHeadsPerWave - 1) / kQHeadsPerWave + 1;
+  const int64_t row = q.heads * kWave;  // 16 B units of one token's q rows
+  return sliced(n, kMaxLaunchWaves / waves_per_token, [&](int64_t s, int64_t m) {
+    QArgs qs = q;
+    qs.in = static_cast<const u32x4 *>(q.in) + s * row;
+    qs.out = static_cast<u32x4 *>(q.out) + s * row;
+    return launch_qkv_slice<kFmt, kNorm>(qs, static_cast<const u32x4 *>(kv) + s * kWave, m, g,
+                                         slots + s, positions + s, cos_sin, max_pos, stream);
+  });
 }
 
 }  // namespace

@@ -7,6 +7,12 @@
 
 namespace kvrec {
 
+// Waves of one kernel launch, at most. A call with more rows runs as several
+// launches on its stream, each over a contiguous slice of the rows (every
+// kernel indexes its rows relative to the pointers it is given), so a grid
+// never approaches the 2^32 work-items one dispatch can cover.
+constexpr int64_t kMaxLaunchWaves = int64_t{1} << 21;
+
 // Geometry of a validated cache (all checks done on the host).
 struct CacheGeom {
   uint8_t *base;

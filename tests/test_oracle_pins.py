@@ -711,3 +711,38 @@ def test_rotation_free_ratio1_does_not_read_positions(record):
     oracle.insert(case.kv_bits[sel], want, 5, case.page_stride, 16, record,
                   case.slot_mapping[sel], None, None, rope="none")
     assert np.array_equal(gated, want)
+
+
+@pytest.mark.parametrize("rope", ["neox", "interleaved", "none"])
+@pytest.mark.parametrize("record", [528, 584])
+@pytest.mark.parametrize("floor", [0.0, 1e-4])
+def test_sanitised_nan_rows_store_zero_records(rope, record, floor):
+    """Rows made only of NaNs (both signs, quiet and signalling payloads),
+    sanitised: every rotated value is NaN and becomes +0, so each group's
+    amax is 0 (or the floor): scale byte 127 (105 with the 1e-4 floor, the
+    smallest e with 1e-4 <= 448 * 2^e being -22), every code 0x00, the legacy
+    tail bf16 +0 and its pad byte 0. At position 0 (cos 1, sin 0) the +0 row
+    rotates to +0 as well and stores the same bytes."""
+    bs, n = 4, 4
+    stride = W.page_stride_for(record, bs)
+    kv = np.array([[[0x7FC0, 0xFFC0, 0x7F81, 0xFFFF][(d + t) % 4] for d in range(512)]
+                   for t in range(n)], np.uint16)
+    slots, pos = np.arange(n), np.zeros(n, np.int64)
+    table = W.rope_table(1)
+    got = np.full(stride, 0xA5, np.uint8)
+    oracle.insert(kv, got, 1, stride, bs, record, slots, pos, table, rope=rope,
+                  amax_floor=floor, sanitize_nans=True)
+    sbyte = 105 if floor else 127
+    if record == 528:
+        assert (got[:n * 512] == 0).all()
+        assert (got[bs * 512:bs * 512 + n * 16] == sbyte).all()
+    else:
+        assert (got[:n * 576] == 0).all()  # 448 codes and the 64 bf16 of each row
+        rows = got[bs * 576:bs * 576 + n * 8].reshape(n, 8)
+        assert (rows[:, :7] == sbyte).all() and (rows[:, 7] == 0).all()
+    zero = np.full(stride, 0xA5, np.uint8)
+    oracle.insert(np.zeros_like(kv), zero, 1, stride, bs, record, slots, pos, table, rope=rope,
+                  amax_floor=floor, sanitize_nans=True)
+    assert np.array_equal(got, zero)
+    assert (got[bs * (512 if record == 528 else 576) + n * (16 if record == 528 else 8):]
+            == 0xA5).all()
