@@ -33,7 +33,7 @@
  *   - Every argument check runs on the host before any launch; on error the
  *     call returns a negative kvrec_status and nothing is launched or
  *     written. The library never throws or aborts across this ABI.
- *   - A call over more than 2^21 waves of work (2^21 tokens of an insert,
+ *   - A call over more than 2^21 waves of work (2^22 tokens of an insert,
  *     2^22 gather rows, 2^21 expansion rows, fewer attention-write tokens)
  *     runs as several kernel launches on `stream`, one per consecutive slice
  *     of the rows, in order. If a later launch fails (KVREC_ERR_HIP), the

@@ -33,6 +33,7 @@
 // Either way the kept blocks end at positions 0 .. n_valid-1 in ascending
 // order, and each lane writes its E outputs.
 #include "kvrec_launch.h"
+#include "kvrec_xcd.h"
 
 namespace kvrec {
 namespace {
@@ -325,17 +326,20 @@ __device__ __forceinline__ void expand_row(const RowInput<E> &in, uint32_t row, 
 
 
 // W waves per block, one row each; each wave has its own LDS share.
+// Blocks are numbered XCD by XCD (xcd_block), so the rows whose ks, ke and
+// end share a cache line run on one XCD and that line is fetched into one L2
+// instead of eight.
 template <int E, int W>
 __global__ __launch_bounds__(W * kWave) void expand_kernel(
     const int32_t *cand, int64_t cand_stride, const int32_t *row_ks, int64_t ks_stride,
     const int32_t *row_ke, int64_t ke_stride, uint32_t rows, int32_t num_candidates,
     int32_t ratio, int32_t sbk, int32_t *sparse, int64_t sparse_stride, int32_t *end,
-    int64_t end_stride) {
+    int64_t end_stride, uint32_t xcd_shift) {
   __shared__ uint2 bitmap[W][kRankWords];
   __shared__ __align__(16) int32_t sorted[W][kWave * E];
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const uint32_t row = blockIdx.x * W + wave;
+  const uint32_t row = xcd_block(xcd_shift) * W + wave;
   if (row >= rows) return;
   const int32_t L = num_candidates * ratio;
   const uint32_t split = static_cast<uint32_t>(ratio) - 1u;  // 1 when each candidate is 2 blocks
@@ -359,11 +363,12 @@ hipError_t launch_expand_e(const ExpandArgs &x, hipStream_t stream) {
   uint32_t rows = static_cast<uint32_t>(x.rows);
   int32_t k = x.num_candidates, ratio = x.ratio, sbk = x.sparse_block;
   int32_t *sparse = x.sparse, *end = x.end;
+  uint32_t xcd_shift = 0;
+  const dim3 grid = xcd_grid<kExpandWaves>(rows, &xcd_shift);
   void *params[] = {&cand, &cs,    &ks,  &kss,    &ke, &kes,    &rows,
-                    &k,    &ratio, &sbk, &sparse, &ss, &end,    &es};
-  const uint32_t blocks = (rows + kExpandWaves - 1) / kExpandWaves;
-  return hipLaunchKernel(reinterpret_cast<const void *>(expand_kernel<E, kExpandWaves>),
-                         dim3(blocks), dim3(kExpandWaves * kWave), params, 0, stream);
+                    &k,    &ratio, &sbk, &sparse, &ss, &end,    &es, &xcd_shift};
+  return hipLaunchKernel(reinterpret_cast<const void *>(expand_kernel<E, kExpandWaves>), grid,
+                         dim3(kExpandWaves * kWave), params, 0, stream);
 }
 
 }  // namespace
@@ -372,23 +377,21 @@ hipError_t launch_expand_e(const ExpandArgs &x, hipStream_t stream) {
 // over consecutive row slices.
 hipError_t launch_expand(const ExpandArgs &x, hipStream_t stream) {
   const int64_t L = static_cast<int64_t>(x.num_candidates) * x.ratio;
-  for (int64_t s = 0; s < x.rows; s += kMaxLaunchWaves) {
+  return sliced(x.rows, kMaxLaunchWaves, [&](int64_t s, int64_t m) {
     ExpandArgs y = x;
-    y.rows = x.rows - s < kMaxLaunchWaves ? x.rows - s : kMaxLaunchWaves;
+    y.rows = m;
     y.cand = x.cand + s * x.cand_stride;
     y.ks = x.ks + s * x.ks_stride;
     y.ke = x.ke + s * x.ke_stride;
     y.sparse = x.sparse + s * x.sparse_stride;
     y.end = x.end + s * x.end_stride;
-    const hipError_t err = L <= 64    ? launch_expand_e<1>(y, stream)
-                           : L <= 128 ? launch_expand_e<2>(y, stream)
-                           : L <= 256 ? launch_expand_e<4>(y, stream)
-                           : L <= 512 ? launch_expand_e<8>(y, stream)
-                           : L <= 1024 ? launch_expand_e<16>(y, stream)
-                                       : hipErrorInvalidValue;
-    if (err != hipSuccess) return err;
-  }
-  return hipSuccess;
+    return L <= 64     ? launch_expand_e<1>(y, stream)
+           : L <= 128  ? launch_expand_e<2>(y, stream)
+           : L <= 256  ? launch_expand_e<4>(y, stream)
+           : L <= 512  ? launch_expand_e<8>(y, stream)
+           : L <= 1024 ? launch_expand_e<16>(y, stream)
+                       : hipErrorInvalidValue;
+  });
 }
 
 }  // namespace kvrec

@@ -14,11 +14,14 @@
 //
 // Shape. The path moves ~1.8 KB per token and does ~2 ALU ops per byte, so it
 // is bound by HBM bandwidth, not by MFMA or VALU throughput: there is no
-// contraction here and no matrix core is used. One wave64 owns one token
+// contraction here and no matrix core is used. One wave64 owns two tokens
 // (the lesson of [KV-only op] 实现拆解 5: with no query heads to iterate,
-// every wave must have a token of its own, or the launch idles most of the
-// chip). On MI355X many short one-row waves also stream faster than fewer
-// waves that loop over rows. Lane l holds latent dims 8l..8l+7:
+// the launch must give every wave tokens of its own, or it idles most of the
+// chip). Each wave issues both tokens' loads before it waits on any, encodes
+// both, then stores both: two tokens per wave keep twice the bytes in flight
+// of one and halve the waves the dispatcher must launch (about 0.2 ns per
+// wave on MI355X, 14.6 us for an empty 65536-wave grid), while three or more
+// need enough registers to cut occupancy. Lane l holds latent dims 8l..8l+7:
 //   - one 16 B global load per lane reads the 1 KB bf16 row, coalesced;
 //   - the 64 RoPE dims 448..511 sit in lanes 56..63, and the NeoX partner of
 //     dim 448+i is 480+i, i.e. lane l ^ 4: one ds_swizzle (xor 4) exchanges
@@ -45,6 +48,7 @@
 // Both take the group's UE8M0 byte as the exponent field of their scale
 // operand, so no separate scaling instruction is needed.
 #include "kvrec_launch.h"
+#include "kvrec_xcd.h"
 
 namespace kvrec {
 namespace {
@@ -174,29 +178,6 @@ __device__ __forceinline__ uint32_t lane_read(uint32_t v, int src_lane) {
   return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src_lane << 2, static_cast<int>(v)));
 }
 
-// Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD
-// b % 8), and each XCD has its own L2. Blocks are renumbered so that each XCD
-// runs chunks of C = 2^xcd_shift consecutive (logical) blocks: the i-th block
-// on XCD x is block ((i / C) * 8 + x) * C + i % C. A chunk keeps the small
-// per-token arrays (slots, positions, indices: 16..32 tokens per 128 B line)
-// and the 8 B / 16 B scale rows of neighbouring tokens in one L2 instead of
-// eight. C is 512 blocks (chunks of 512 measured 1-2% faster than one
-// contiguous range per XCD for single launches on clean caches: insert 89.7
-// -> 87.5 us, gather 68.4 -> 66.9 us at 262144 tokens; the same back to back;
-// chunks of 4096 made the gather slower, 72 us, and the insert + gather step
-// took 139.5 us with chunks of 512 against 140-142 with 256 or 1024), or for
-// grids of up to
-// 8 * 512 blocks the power of two that gives each XCD one chunk. The grid is
-// padded to whole chunks on every XCD; the padding blocks find no work.
-constexpr int kXcds = 8;
-constexpr uint32_t kXcdChunkShift = 9;  // 512 blocks
-
-__device__ __forceinline__ uint32_t xcd_block(uint32_t xcd_shift) {
-  const uint32_t b = blockIdx.x;
-  const uint32_t x = b % kXcds, i = b / kXcds;
-  return (((i >> xcd_shift) * kXcds + x) << xcd_shift) + (i & ((1u << xcd_shift) - 1u));
-}
-
 // Largest |x| of this lane's 8 values, as fp32 bits (compares as unsigned
 // integers because every value is finite and non-negative).
 __device__ __forceinline__ uint32_t lane_amax_bits(const float f[8]) {
@@ -308,13 +289,21 @@ __device__ __forceinline__ void rope_interleaved(float f[8], int lane, const f32
   }
 }
 
-// Encode one loaded token and store its record. `raw` is the lane's 16 B of
-// the bf16 row, c0..s1 the lane's cos/sin values (lanes 56..63 only).
-template <int P, int kFmt, int kRope, bool kSanitize, bool kOptions>
-__device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, const u32x4 raw,
-                                             const f32x4 c0, const f32x4 c1, const f32x4 s0,
-                                             const f32x4 s1, uint32_t slot,
-                                             uint32_t amax_floor_bits, float fp8_scale) {
+// One token's record, encoded and held in registers until it is stored:
+// this lane's 16 B of the row (8 codes in v.x, v.y for the MXFP8 and fp8
+// formats and the legacy NoPE lanes; 8 bf16 in v for the bf16 format and the
+// legacy tail lanes) and the packed scale bytes of the lanes that store them.
+struct Encoded {
+  u32x4 v;
+  uint32_t w;
+};
+
+// Encode one loaded token. `raw` is the lane's 16 B of the bf16 row, c0..s1
+// the lane's cos/sin values (lanes 56..63 only).
+template <int kFmt, int kRope, bool kSanitize, bool kOptions>
+__device__ __forceinline__ Encoded encode(int lane, const u32x4 raw, const f32x4 c0,
+                                          const f32x4 c1, const f32x4 s0, const f32x4 s1,
+                                          uint32_t amax_floor_bits, float fp8_scale) {
   constexpr bool kLegacy = kFmt == kFmtLegacy;
   float f[8];
   unpack_bf16x8(raw, f);
@@ -324,25 +313,21 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
 #pragma unroll
     for (int k = 0; k < 8; ++k) f[k] = f[k] == f[k] ? f[k] : 0.0f;  // NaN -> +0
   }
-  const PageOff po = page_of(slot, a.block_size, a.div_magic, a.div_shift);
-  const uint32_t off = po.off;
-  uint8_t *page = a.base + static_cast<int64_t>(po.page) * a.page_stride;
-  constexpr bool nt_data = (P & kNtData) != 0;
-  constexpr bool nt_scale = (P & kNtScale) != 0;
+  Encoded e;
+  asm("" : "=v"(e.w));  // only the lanes that store scale bytes set it
 
   if constexpr (kFmt == kFmtBf16) {
     // Non-packed bf16 cache ([KV-only op] 实现拆解 1): the 1 KB row at
     // page + off*1024. The NoPE lanes store their input bits unchanged (the
     // exact bf16 of an exact widening); the tail lanes round the rotation.
-    u32x4 h = raw;
+    e.v = raw;
     if (lane >= 56) {
-      h.x = pack_bf16x2(f[0], f[1]);
-      h.y = pack_bf16x2(f[2], f[3]);
-      h.z = pack_bf16x2(f[4], f[5]);
-      h.w = pack_bf16x2(f[6], f[7]);
+      e.v.x = pack_bf16x2(f[0], f[1]);
+      e.v.y = pack_bf16x2(f[2], f[3]);
+      e.v.z = pack_bf16x2(f[4], f[5]);
+      e.v.w = pack_bf16x2(f[6], f[7]);
     }
-    st<nt_data>(reinterpret_cast<u32x4 *>(page + off * 1024u + lane * 16), h);
-    return;
+    return e;
   }
   if constexpr (kFmt == kFmtFp8) {
     // Non-packed fp8 cache with one fp32 per-tensor scale: the 512 B row at
@@ -385,8 +370,9 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
       for (int k = 0; k < 8; ++k)
         y[k] = __builtin_amdgcn_fmed3f(__fdiv_rn(f[k], s), -448.0f, 448.0f);
     }
-    st<nt_data>(reinterpret_cast<u32x2 *>(page + off * 512u + lane * 8), encode_e4m3x8(y, 127u));
-    return;
+    const u32x2 c = encode_e4m3x8(y, 127u);
+    e.v = u32x4{c.x, c.y, 0u, 0u};
+    return e;
   }
 
   uint32_t amax = lane_amax_bits(f);
@@ -394,36 +380,27 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
   amax = dpp_umax<kQuadXor2>(amax);
   if constexpr (kLegacy) amax = dpp_umax<kHalfRowMirror>(amax);  // 8 lanes = 64 dims
   if constexpr (kOptions) amax = max(amax, amax_floor_bits);  // the compressed-KV floor
-  const int e = scale_exponent(amax);
-  const uint32_t b = static_cast<uint32_t>(e + 127);
+  const int ex = scale_exponent(amax);
+  const uint32_t b = static_cast<uint32_t>(ex + 127);
 
   if constexpr (!kLegacy) {
-    // MXFP8 record, 528 B: 512 codes at page + off*512, 16 scale bytes at
-    // page + block_size*512 + off*16 ([MXFP8 record] 功能与动机, 关键源码片段).
-    st<nt_data>(reinterpret_cast<u32x2 *>(page + off * 512u + lane * 8), encode_e4m3x8(f, b));
-    // Scale byte of group g lives in lanes 4g..4g+3; lane 16k gathers groups
-    // 4k..4k+3 from lanes 16k, 16k+4, 16k+8, 16k+12 and stores them as a dword.
-    const uint32_t word =
-        b | (dpp<kRowShl4>(b) << 8) | (dpp<kRowShl8>(b) << 16) | (dpp<kRowShl12>(b) << 24);
-    if ((lane & 15) == 0)
-      st<nt_scale>(
-          reinterpret_cast<uint32_t *>(page + a.block_size * 512u + off * 16u + (lane >> 2)),
-          word);
+    // MXFP8 record: 512 codes. Scale byte of group g lives in lanes
+    // 4g..4g+3; lane 16k gathers groups 4k..4k+3 from lanes 16k, 16k+4,
+    // 16k+8, 16k+12 into one dword.
+    const u32x2 c = encode_e4m3x8(f, b);
+    e.v = u32x4{c.x, c.y, 0u, 0u};
+    e.w = b | (dpp<kRowShl4>(b) << 8) | (dpp<kRowShl8>(b) << 16) | (dpp<kRowShl12>(b) << 24);
   } else {
-    // Legacy record, 584 B: a 576 B data row (448 codes of dims 0..447, then
-    // the 64 rotated tail dims as little-endian bf16) at page + off*576, and
-    // an 8 B scale row (7 scales over 64-dim groups, then a 0 pad byte) at
-    // page + block_size*576 + off*8 ([MXFP8 record] 功能与动机).
-    uint8_t *row = page + off * 576u;
+    // Legacy record: 448 codes of dims 0..447 (lanes 0..55), then the 64
+    // rotated tail dims as little-endian bf16 (lanes 56..63).
     if (lane < 56) {
-      st<nt_data>(reinterpret_cast<u32x2 *>(row + lane * 8), encode_e4m3x8(f, b));
+      const u32x2 c = encode_e4m3x8(f, b);
+      e.v = u32x4{c.x, c.y, 0u, 0u};
     } else {
-      u32x4 h;
-      h.x = pack_bf16x2(f[0], f[1]);
-      h.y = pack_bf16x2(f[2], f[3]);
-      h.z = pack_bf16x2(f[4], f[5]);
-      h.w = pack_bf16x2(f[6], f[7]);
-      st<nt_data>(reinterpret_cast<u32x4 *>(row + 448 + (lane - 56) * 16), h);
+      e.v.x = pack_bf16x2(f[0], f[1]);
+      e.v.y = pack_bf16x2(f[2], f[3]);
+      e.v.z = pack_bf16x2(f[4], f[5]);
+      e.v.w = pack_bf16x2(f[6], f[7]);
     }
     // Scale byte of group g lives in lanes 8g..8g+7. Lane 0 packs groups
     // 0..3 (lanes 0, 8, 16, 24), lane 32 packs groups 4..6 and the pad byte.
@@ -431,12 +408,59 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
     const uint32_t b2 = lane_read(b, (lane + 16) & 63);
     const uint32_t r3 = lane_read(b, (lane + 24) & 63);
     const uint32_t b3 = lane == 32 ? 0u : r3;
-    const uint32_t word = b | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    e.w = b | (b1 << 8) | (b2 << 16) | (b3 << 24);
+  }
+  return e;
+}
+
+// Store an encoded token at its slot ([MXFP8 record] 功能与动机, 实现拆解 4,
+// 关键源码片段: each page holds its data rows, then its scale rows).
+//   MXFP8, 528 B: 512 codes at page + off*512, 16 scale bytes at
+//     page + block_size*512 + off*16.
+//   Legacy, 584 B: a 576 B data row (448 codes, then 64 bf16) at
+//     page + off*576, an 8 B scale row (7 scales, then a 0 pad byte) at
+//     page + block_size*576 + off*8.
+//   bf16 / fp8 rows: page + off*1024 / page + off*512, no scale region.
+template <int P, int kFmt>
+__device__ __forceinline__ void store_record(const InsertArgs &a, int lane, uint32_t slot,
+                                             const Encoded &e) {
+  const PageOff po = page_of(slot, a.block_size, a.div_magic, a.div_shift);
+  const uint32_t off = po.off;
+  uint8_t *page = a.base + static_cast<int64_t>(po.page) * a.page_stride;
+  constexpr bool nt_data = (P & kNtData) != 0;
+  constexpr bool nt_scale = (P & kNtScale) != 0;
+  if constexpr (kFmt == kFmtBf16) {
+    st<nt_data>(reinterpret_cast<u32x4 *>(page + off * 1024u + lane * 16), e.v);
+  } else if constexpr (kFmt == kFmtFp8) {
+    st<nt_data>(reinterpret_cast<u32x2 *>(page + off * 512u + lane * 8), u32x2{e.v.x, e.v.y});
+  } else if constexpr (kFmt == kFmtMxfp8) {
+    st<nt_data>(reinterpret_cast<u32x2 *>(page + off * 512u + lane * 8), u32x2{e.v.x, e.v.y});
+    if ((lane & 15) == 0)
+      st<nt_scale>(
+          reinterpret_cast<uint32_t *>(page + a.block_size * 512u + off * 16u + (lane >> 2)),
+          e.w);
+  } else {
+    uint8_t *row = page + off * 576u;
+    if (lane < 56)
+      st<nt_data>(reinterpret_cast<u32x2 *>(row + lane * 8), u32x2{e.v.x, e.v.y});
+    else
+      st<nt_data>(reinterpret_cast<u32x4 *>(row + 448 + (lane - 56) * 16), e.v);
     if ((lane & 31) == 0)
       st<nt_scale>(
           reinterpret_cast<uint32_t *>(page + a.block_size * 576u + off * 8u + (lane >> 3)),
-          word);
+          e.w);
   }
+}
+
+template <int P, int kFmt, int kRope, bool kSanitize, bool kOptions>
+__device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, const u32x4 raw,
+                                             const f32x4 c0, const f32x4 c1, const f32x4 s0,
+                                             const f32x4 s1, uint32_t slot,
+                                             uint32_t amax_floor_bits, float fp8_scale) {
+  store_record<P, kFmt>(
+      a, lane, slot,
+      encode<kFmt, kRope, kSanitize, kOptions>(lane, raw, c0, c1, s0, s1, amax_floor_bits,
+                                               fp8_scale));
 }
 
 // Lanes 56..63 read the cos/sin values of table row `row` that they use:
@@ -483,12 +507,13 @@ __device__ __forceinline__ void insert_wave(const InsertArgs &a, uint32_t t0, in
   int64_t sl[T], ps[T];
 #pragma unroll
   for (int k = 0; k < T; ++k) {
-    const uint32_t t = t0 + k;
-    const bool in = (T == 1) || t < a.n;
-    raw[k] = in ? ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t) * kWave + lane)
-                : u32x4{0, 0, 0, 0};
-    sl[k] = in ? a.slots[t] : -1;
-    ps[k] = !has_pos ? 0 : in ? a.positions[t] : -1;
+    // A token past the end reloads the last one and is then skipped: the
+    // loads stay unconditional, so no loaded register is copied through a
+    // branch (a copy would wait for the load before the next is issued).
+    const uint32_t t = (T == 1 || t0 + k < a.n) ? t0 + k : a.n - 1;
+    raw[k] = ld<(P & kNtKv) != 0>(a.kv + static_cast<uint64_t>(t) * kWave + lane);
+    sl[k] = a.slots[t];
+    ps[k] = has_pos ? a.positions[t] : 0;
   }
   // All three loads are issued before anything waits on the slot or position.
   __builtin_amdgcn_sched_barrier(0);
@@ -506,7 +531,10 @@ __device__ __forceinline__ void insert_wave(const InsertArgs &a, uint32_t t0, in
   bool ok[T];
 #pragma unroll
   for (int k = 0; k < T; ++k) {
-    ok[k] = below(sl[k], a.total_slots) && (!has_pos || below(ps[k], a.max_pos));
+    // Bitwise, not short-circuit: a branch here would let the compiler sink
+    // a position load behind the wait for the slot.
+    ok[k] = (T == 1 || t0 + k < a.n) & below(sl[k], a.total_slots) &
+            (!has_pos || below(ps[k], a.max_pos));
     slot[k] = static_cast<uint32_t>(sl[k]);
     row[k] = static_cast<uint32_t>(ps[k]);
   }
@@ -526,11 +554,18 @@ __device__ __forceinline__ void insert_wave(const InsertArgs &a, uint32_t t0, in
     asm("" : "=v"(c0[k]), "=v"(c1[k]), "=v"(s0[k]), "=v"(s1[k]));
     if (ok[k]) load_table<P, kRope>(a.cos_sin, row[k], lane, c0[k], c1[k], s0[k], s1[k]);
   }
+  // Every token is encoded before any is stored: a store issued between two
+  // encodes would make the second one wait for the store to complete (the
+  // wait counter covers loads and stores alike).
+  Encoded e[T];
 #pragma unroll
   for (int k = 0; k < T; ++k)
     if (ok[k])
-      encode_store<P, kFmt, kRope, kSanitize, kOptions>(a, lane, raw[k], c0[k], c1[k], s0[k],
-                                                        s1[k], slot[k], amax_floor_bits, scale);
+      e[k] = encode<kFmt, kRope, kSanitize, kOptions>(lane, raw[k], c0[k], c1[k], s0[k], s1[k],
+                                                      amax_floor_bits, scale);
+#pragma unroll
+  for (int k = 0; k < T; ++k)
+    if (ok[k]) store_record<P, kFmt>(a, lane, slot[k], e[k]);
 }
 
 template <int P, int W, int T, int kFmt, int kRope, bool kSanitize, bool kOptions>
@@ -789,7 +824,11 @@ __global__ __launch_bounds__(W * kWave) void gather_kernel(
 // cached except for the bf16 cache (insert_policy below). The
 // gather's bf16 output is non-temporal: written once, and as large as the
 // Infinity Cache, it would otherwise evict the records. One wave per insert
-// block; two rows per gather wave, two waves per block.
+// block, two tokens per wave (single launches on clean caches, kernel
+// timestamps: MXFP8 262144 contiguous 86.6 -> 80.4 us, legacy 65536 random
+// 25.5 -> 23.7 us, fp8 cache 88.6 -> 79.6 us, bf16 cache 94.7 -> 91.2 us;
+// back to back the same or faster; three tokens per wave lose occupancy and
+// were slower everywhere); two rows per gather wave, two waves per block.
 // Cache policy of the insert per format (measured on MI355X, back to back at
 // 262144 tokens): the kv rows non-temporal and the cos/sin rows cached took
 // the MXFP8 insert from 84.7 to 80.5 us (legacy 84 -> 80, fp8 102 -> 98, the
@@ -800,7 +839,7 @@ constexpr int insert_policy() {
   return kFmt == kFmtBf16 ? (kNtKv | kNtTable) : kNtKv;
 }
 constexpr int kInsertWaves = 1;   // waves per block
-constexpr int kInsertTokens = 1;  // tokens per wave
+constexpr int kInsertTokens = 2;  // tokens per wave
 constexpr int kGatherPolicy = kNtOut;
 constexpr int kGatherWaves = 2;
 // q rows (heads) per wave of the attention write. Measured on MI355X at 4096
@@ -817,31 +856,6 @@ void division_magic32(uint32_t d, uint32_t *magic, uint32_t *shift) {
   *shift = l;
 }
 constexpr int kGatherRows = 2;    // rows per wave
-
-// Grid of `waves` (>= 1) waves in blocks of W, padded to whole chunks on
-// every XCD, and the chunk's log2 (see xcd_block).
-template <int W>
-dim3 xcd_grid(int64_t waves, uint32_t *xcd_shift) {
-  const int64_t blocks = (waves + W - 1) / W;
-  const int64_t per_xcd = (blocks + kXcds - 1) / kXcds;
-  uint32_t shift = 0;
-  while (shift < kXcdChunkShift && (int64_t{1} << shift) < per_xcd) ++shift;
-  const int64_t chunk = int64_t{1} << shift;
-  const int64_t chunks = (blocks + kXcds * chunk - 1) / (kXcds * chunk);
-  *xcd_shift = shift;
-  return dim3(static_cast<uint32_t>(chunks * chunk * kXcds));
-}
-
-// Runs launch(first_row, rows) over consecutive slices of at most `slice`
-// rows, stopping at the first launch error.
-template <typename F>
-hipError_t sliced(int64_t n, int64_t slice, F launch) {
-  for (int64_t s = 0; s < n; s += slice) {
-    const hipError_t err = launch(s, n - s < slice ? n - s : slice);
-    if (err != hipSuccess) return err;
-  }
-  return hipSuccess;
-}
 
 template <int P, int W, int T, int kFmt, int kRope, bool kSanitize, bool kOptions>
 hipError_t launch_insert_slice(const void *kv, int64_t n, const CacheGeom &g,
@@ -1035,10 +1049,10 @@ hipError_t launch_insert(const void *kv, int64_t n, const CacheGeom &g, const in
 #undef KVREC_PLAIN
   if (format != Format::kMxfp8 && format != Format::kLegacy) return hipErrorInvalidValue;
   const bool legacy = format == Format::kLegacy;
-  // Ratio R > 1: the gated group kernel. Ratio 1: one wave per token, as
-  // for the plain insert (measured on MI355X at 262144 tokens, groups of 2 or
-  // 4 tokens took 89-91 us for NeoX + sanitise against 81 us per token, and
-  // won under 2 us for the interleaved rotation).
+  // Ratio R > 1: the gated group kernel. Ratio 1: the plain insert's
+  // kernel shape with the options (measured on MI355X at 262144 tokens, the
+  // gated group kernel without its gate took 89-91 us for NeoX + sanitise
+  // against 81 us for one wave per token).
 #define KVREC_INSERT(L, R, S)                                                                   \
   if (legacy == (L == kFmtLegacy) && o.rope == R && o.sanitize == S) {                          \
     if (o.ratio > 1)                                                                            \

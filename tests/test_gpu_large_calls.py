@@ -21,7 +21,8 @@ from tests import parity_util as P
 
 pytestmark = pytest.mark.gpu
 
-LAUNCH_WAVES = 2 ** 21  # waves per launch (one wave per insert token)
+LAUNCH_WAVES = 2 ** 21  # waves per launch
+INSERT_TOKENS_PER_WAVE = 2
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -65,7 +66,8 @@ def _records_equal_oracle(backing: torch.Tensor, record: int, bs: int, stride: i
 
 @pytest.mark.parametrize("record", [528, 584])
 def test_insert_over_one_launch(record):
-    n, bs = LAUNCH_WAVES + 37, 64
+    per_launch = LAUNCH_WAVES * INSERT_TOKENS_PER_WAVE
+    n, bs = per_launch + 37, 64
     stride = W.page_stride_for(record, bs)
     nb = (n + n // 50) // bs + 1
     g = _gen(71 + record)
@@ -80,12 +82,12 @@ def test_insert_over_one_launch(record):
     one.zero_()
     two.zero_()
     B.kvrec_insert(kv, k_one, slots, positions, cs, bs)
-    m = LAUNCH_WAVES // 2 + 11
+    m = per_launch // 2 + 11
     B.kvrec_insert(kv[:m], k_two, slots[:m], positions[:m], cs, bs)
     B.kvrec_insert(kv[m:], k_two, slots[m:], positions[m:], cs, bs)
     torch.cuda.synchronize()
     assert torch.equal(one, two)
-    edge = slice(LAUNCH_WAVES - 40, LAUNCH_WAVES + 37)
+    edge = slice(per_launch - 40, per_launch + 37)
     assert _records_equal_oracle(one, record, bs, stride, kv, slots, positions, table, edge) > 60
 
 
