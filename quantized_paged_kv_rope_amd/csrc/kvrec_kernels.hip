@@ -219,18 +219,37 @@ __device__ __forceinline__ u32x2 encode_e4m3x8(const float f[8], uint32_t scale_
   return u32x2{__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1)};
 }
 
-// Rotate the tail dims held by lanes 56..63 in place. All lanes must call it
-// (the swizzle needs the whole wave); lanes < 56 keep their values.
-//   lanes 56..59 hold x1 = dims 448+i, lanes 60..63 hold x2 = dims 480+i,
-//   i = 8*(lane & 3) + k; cos = row[i], sin = row[32 + i].
+// The NeoX table values of a tail lane. Lanes 56..59 hold x1 = dims 448+i
+// and lanes 60..63 x2 = dims 480+i, i = 8*(lane & 3) + k, and both lanes of
+// a pair (lane, lane ^ 4) need cos = row[i] and sin = row[32 + i]. Each lane
+// loads one half of the row's 256 B once (load_table: lanes 56..59 the cos
+// values, 60..63 the sin values, 32 B each), and the pair swaps halves by
+// ds_swizzle (xor 4). Measured on MI355X against every tail lane loading all
+// 64 B it uses (each half twice): 80.2 -> 69.8 us for 262144 MXFP8 tokens on
+// clean caches. All lanes must call it (the swizzle needs the whole wave).
+__device__ __forceinline__ void neox_table(int lane, const f32x4 h0, const f32x4 h1, float c[8],
+                                           float s[8]) {
+  const float own[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+  const bool second = (lane & 4) != 0;  // this lane holds x2 and loaded the sin values
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float other = __uint_as_float(static_cast<uint32_t>(
+        __builtin_amdgcn_ds_swizzle(static_cast<int>(__float_as_uint(own[k])), kSwizzleXor4)));
+    c[k] = second ? other : own[k];
+    s[k] = second ? own[k] : other;
+  }
+}
+
+// Rotate the tail dims held by lanes 56..63 in place (c, s from neox_table).
+// All lanes must call it (the swizzle needs the whole wave); lanes < 56 keep
+// their values.
 //   r1 = x1*c - x2*s,  r2 = x2*c + x1*s  (each operation rounded separately)
 //   With kScaled, the values are x * inv (the q side's normalised rows): the
 //   partner's raw bf16 values are multiplied by the same inv, exactly as the
 //   partner lane scales its own.
 template <bool kScaled = false>
-__device__ __forceinline__ void rope_tail(float f[8], const u32x4 raw, int lane, const f32x4 c0,
-                                          const f32x4 c1, const f32x4 s0, const f32x4 s1,
-                                          float inv = 1.0f) {
+__device__ __forceinline__ void rope_tail(float f[8], const u32x4 raw, int lane, const float c[8],
+                                          const float s[8], float inv = 1.0f) {
   // Partner lane l ^ 4 by ds_swizzle (bit-mask mode, no VALU issue: two DPP
   // moves per dword would add 8 VALU instructions, which the fp8 cache's
   // division-heavy insert measurably pays for).
@@ -246,8 +265,6 @@ __device__ __forceinline__ void rope_tail(float f[8], const u32x4 raw, int lane,
 #pragma unroll
       for (int k = 0; k < 8; ++k) g[k] = g[k] * inv;
     }
-    const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
     const bool second = (lane & 4) != 0;  // this lane holds x2 (dims 480..)
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -307,7 +324,11 @@ __device__ __forceinline__ Encoded encode(int lane, const u32x4 raw, const f32x4
   constexpr bool kLegacy = kFmt == kFmtLegacy;
   float f[8];
   unpack_bf16x8(raw, f);
-  if constexpr (kRope == kRopeNeox) rope_tail(f, raw, lane, c0, c1, s0, s1);
+  if constexpr (kRope == kRopeNeox) {
+    float c[8], sn[8];
+    neox_table(lane, c0, c1, c, sn);
+    rope_tail(f, raw, lane, c, sn);
+  }
   if constexpr (kRope == kRopeInterleaved) rope_interleaved(f, lane, c0, s0);
   if constexpr (kSanitize) {
 #pragma unroll
@@ -463,10 +484,11 @@ __device__ __forceinline__ void encode_store(const InsertArgs &a, int lane, cons
                                                fp8_scale));
 }
 
-// Lanes 56..63 read the cos/sin values of table row `row` that they use:
-// NeoX lane 56+j takes cos[8(j&3) .. +7] and sin[8(j&3) .. +7]; interleaved
-// lane 56+j takes cos[4j .. 4j+3] and sin[4j .. 4j+3]. Other lanes load
-// nothing.
+// Lanes 56..63 read the cos/sin values of table row `row`. NeoX: lane 56+j
+// (j < 4) loads cos[8j .. 8j+7] and lane 60+j loads sin[8j .. 8j+7] into c0,
+// c1 (neox_table then swaps halves within the pair; s0, s1 stay unused).
+// Interleaved: lane 56+j takes cos[4j .. 4j+3] (c0) and sin[4j .. 4j+3]
+// (s0). Other lanes load nothing.
 template <int P, int kRope>
 __device__ __forceinline__ void load_table(const f32x4 *cos_sin, uint32_t row, int lane,
                                            f32x4 &c0, f32x4 &c1, f32x4 &s0, f32x4 &s1) {
@@ -474,11 +496,10 @@ __device__ __forceinline__ void load_table(const f32x4 *cos_sin, uint32_t row, i
   const f32x4 *tab = cos_sin + static_cast<uint64_t>(row) * 16;
   constexpr bool nt = (P & kNtTable) != 0;
   if constexpr (kRope == kRopeNeox) {
-    const int q = 2 * (lane & 3);  // float4 index of cos[8*(lane&3)]
+    // float4 index of cos[8*(lane&3)] (lanes 56..59) or sin[8*(lane&3)]
+    const int q = 2 * (lane & 3) + ((lane & 4) ? 8 : 0);
     c0 = ld<nt>(tab + q);
     c1 = ld<nt>(tab + q + 1);
-    s0 = ld<nt>(tab + 8 + q);
-    s1 = ld<nt>(tab + 9 + q);
   } else {
     c0 = ld<nt>(tab + (lane - 56));      // cos of pairs 4j..4j+3
     s0 = ld<nt>(tab + 8 + (lane - 56));  // sin of the same pairs
@@ -625,6 +646,8 @@ __device__ __forceinline__ void qnorm_rope_wave(const InsertArgs &a, const u32x4
 #pragma unroll
   for (int k = 0; k < HPW; ++k)
     if (h0 + k < heads) raw[k] = ld<(P & kNtKv) != 0>(q_in + (row0 + k) * kWave + lane);
+  float c[8], sn[8];
+  neox_table(lane, c0, c1, c, sn);  // once per token, for every head
 #pragma unroll
   for (int k = 0; k < HPW; ++k) {
     if (h0 + k >= heads) break;
@@ -640,7 +663,7 @@ __device__ __forceinline__ void qnorm_rope_wave(const InsertArgs &a, const u32x4
 #pragma unroll
       for (int j = 0; j < 8; ++j) f[j] = f[j] * inv;
     }
-    rope_tail<kNorm>(f, raw[k], lane, c0, c1, s0, s1, inv);
+    rope_tail<kNorm>(f, raw[k], lane, c, sn, inv);
     u32x4 h;
     h.x = pack_bf16x2(f[0], f[1]);
     h.y = pack_bf16x2(f[2], f[3]);
