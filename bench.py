@@ -175,22 +175,25 @@ def _time_cold(fn, flush, reps=50):
     return np.array(ts)
 
 
-def _time_back_to_back(fn, reps=100):
-    """Launches issued back to back on the current stream, each between its
-    own pair of HIP events (the headline's protocol)."""
+def _time_back_to_back(fn, batches=10, per_batch=20):
+    """Launches issued back to back on the current stream: `batches` runs of
+    `per_batch` launches, one pair of HIP events around each run; the time
+    per launch of each run (its kernels and the gaps between them, without
+    an event between every two launches)."""
     import torch
 
     for _ in range(5):
         fn()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
+          for _ in range(batches)]
     torch.cuda.synchronize()
     for e0, e1 in ev:
         e0.record()
-        fn()
+        for _ in range(per_batch):
+            fn()
         e1.record()
     torch.cuda.synchronize()
-    return np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+    return np.array([e0.elapsed_time(e1) * 1e3 / per_batch for e0, e1 in ev])
 
 
 TARGET_FRAC = 0.70
@@ -213,10 +216,11 @@ def _target_row(workload, op, rows, valid, nbytes, cold, b2b):
 
 
 def target_rows(dev, prefill) -> list:
-    """Every kernel the >= 70% target covers, timed cold (median of 50) and
-    back to back (median of 100): the 262144-token insert and gather (the
-    headline's tensors), the 65536-token 584 B insert (random slots, 5% -1)
-    and the 64 x 2048 top-k gather from the 32768-page cache."""
+    """Every kernel the >= 70% target covers, timed cold (median of 50
+    single launches) and back to back (median over 10 runs of 20 launches):
+    the 262144-token insert and gather (the headline's tensors), the
+    65536-token 584 B insert (random slots, 5% -1) and the 64 x 2048 top-k
+    gather from the 32768-page cache."""
     import torch
 
     from quantized_paged_kv_rope_amd import binding as B

@@ -54,6 +54,9 @@ namespace kvrec {
 namespace {
 
 constexpr int kWave = 64;
+// s_waitcnt immediate (gfx9 encoding) that waits for every outstanding vector
+// memory operation and nothing else: vmcnt 0, expcnt 7, lgkmcnt 15.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // DPP controls (gfx9 encoding).
 constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
@@ -575,6 +578,13 @@ __device__ __forceinline__ void insert_wave(const InsertArgs &a, uint32_t t0, in
     asm("" : "=v"(c0[k]), "=v"(c1[k]), "=v"(s0[k]), "=v"(s1[k]));
     if (ok[k]) load_table<P, kRope>(a.cos_sin, row[k], lane, c0[k], c1[k], s0[k], s1[k]);
   }
+  // Every load of the wave is needed before the first encode. Waiting for all
+  // of them here, in one place every path passes, tells the compiler's wait
+  // insertion that nothing is outstanding afterwards; left to itself it put a
+  // conservative full wait before the second token's stores, which made them
+  // wait for the first token's stores to complete (measured on MI355X, legacy
+  // 65536 random tokens on clean caches: 24.1 -> 22.4 us).
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   // Every token is encoded before any is stored: a store issued between two
   // encodes would make the second one wait for the store to complete (the
   // wait counter covers loads and stores alike).
