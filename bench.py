@@ -9,10 +9,10 @@ Prints ONE JSON line: tokens/s through the path, per-kernel durations from
 HIP events recorded on the stream the kernels run on, the dominant kernel's
 achieved bandwidth against the 8 TB/s HBM peak, every kernel the 70% target
 covers ("target_rows": the 262144-token insert and gather, the 65536-token
-584 B insert and the 64 x 2048 top-k gather, each timed cold and back to
-back), and the CPU oracle timed on a bounded sample of the same workload
-(single-threaded, median of 3, and on all the host threads it is given,
-the two results asserted identical).
+584 B insert and the 64 x 2048 top-k gather, each timed cold, back to back
+over copies of its buffers, and back to back), and the CPU oracle timed on
+a bounded sample of the same workload (single-threaded, median of 3, and on
+all the host threads it is given, the two results asserted identical).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--no-target-rows]
