@@ -557,8 +557,9 @@ __device__ __forceinline__ void insert_wave(const InsertArgs &a, uint32_t t0, in
   for (int k = 0; k < T; ++k) {
     // Bitwise, not short-circuit: a branch here would let the compiler sink
     // a position load behind the wait for the slot.
-    ok[k] = (T == 1 || t0 + k < a.n) & below(sl[k], a.total_slots) &
-            (!has_pos || below(ps[k], a.max_pos));
+    ok[k] = static_cast<bool>(static_cast<unsigned>(T == 1 || t0 + k < a.n) &
+                              static_cast<unsigned>(below(sl[k], a.total_slots)) &
+                              static_cast<unsigned>(!has_pos || below(ps[k], a.max_pos)));
     slot[k] = static_cast<uint32_t>(sl[k]);
     row[k] = static_cast<uint32_t>(ps[k]);
   }
